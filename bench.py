@@ -1,0 +1,213 @@
+#!/usr/bin/env python3
+"""Benchmark: MoE-LoRA layer fwd+bwd tokens/s on one MI355X.
+
+One step = route + forward + backward of the Qwen3-30B-A3B-shaped layer
+(T=4096, d=2048, n=768, E=128, top-8, LoRA rank 64 on gate_up and down, bf16,
+router logits N(0,1)) on seeded synthetic inputs already resident in HBM.
+
+Prints ONE JSON line.  Besides the driver's fields it carries
+  roofline      the dominant kernel (the gate_up grouped GEMM) against its
+                bound, from HIP-event timing of every launch over a second
+                timed region of the same steps;
+  gemm_mfma_frac  algorithmic grouped-GEMM FLOPs / summed GEMM kernel time /
+                bf16 dense MFMA peak;
+  kernels_us    average duration per kernel;
+  cpu_baseline  the CPU oracle timed on a bounded sample of the same workload.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "MoE-LoRA layer fwd+bwd tokens/s; grouped-GEMM % of bf16 MFMA peak"
+PEAK_BF16 = 2516.6e12   # MI355X dense bf16 MFMA, FLOP/s
+PEAK_HBM = 8.0e12       # MI355X HBM3E, B/s
+GEMM_KERNELS = ("gate_up", "down", "dh", "dx", "prepass_xa", "prepass_ha", "prepass_qdn",
+                "prepass_qgu", "grad_db_dn", "grad_da_dn", "grad_db_gu", "grad_da_gu")
+
+
+def kernel_work(c):
+    """Algorithmic FLOPs and unique HBM bytes of one launch of each kernel.
+
+    Bytes count every input read once and every output written once (bf16 =
+    2 B, fp32 = 4 B); re-reads of gathered rows are cache traffic, not
+    algorithmic bytes."""
+    T, d, n, r, k, S = c.T, c.d, c.n, c.r, c.k, c.n_shared
+    P = T * k + S * T
+    Et = c.E + S
+    b = 2
+    W_gu, W_dn = Et * 2 * n * d * b, Et * d * n * b
+    A_gu, B_gu, A_dn, B_dn = Et * d * r * b, Et * r * 2 * n * b, Et * n * r * b, Et * r * d * b
+    X = T * d * b
+    G, H, R, O = P * 2 * n * b, P * n * b, P * r * b, P * d * b
+    idx = P * 4 * 2
+    return {
+        "prepass_xa": (2 * P * d * r, X + A_gu + R + idx),
+        "gate_up": (2 * P * d * 2 * n + 2 * P * r * 2 * n, W_gu + B_gu + X + R + G + H + idx),
+        "prepass_ha": (2 * P * n * r, H + A_dn + R),
+        "down": (2 * P * n * d + 2 * P * r * d, W_dn + B_dn + H + R + O),
+        "combine_y": (2 * P * d, O + T * d * b + idx),
+        "prepass_qdn": (2 * P * d * r, X + B_dn + R + idx),
+        "dh": (2 * P * d * n + 2 * P * r * n, W_dn + A_dn + X + R + 2 * G + idx),
+        "prepass_qgu": (2 * P * 2 * n * r, G + B_gu + R),
+        "dx": (2 * P * 2 * n * d + 2 * P * r * d, W_gu + A_gu + G + R + O),
+        "combine_dx": (P * d, O + T * d * b + idx),
+        "grad_db_dn": (2 * P * r * d, R + X + Et * r * d * 4 + idx),
+        "grad_da_dn": (2 * P * n * r, H + R + Et * n * r * 4),
+        "grad_db_gu": (2 * P * r * 2 * n, R + G + Et * r * 2 * n * 4),
+        "grad_da_gu": (2 * P * d * r, X + R + Et * d * r * 4 + idx),
+    }
+
+
+def cpu_baseline(dims, inp, budget_s: float):
+    """The oracle (float32, numpy) on the first T_s tokens of the same inputs:
+    route + forward + backward; tokens/s = T_s / wall time."""
+    import dataclasses
+
+    import numpy as np
+    import oracle
+
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [os.cpu_count()])
+    except Exception:  # pragma: no cover
+        threads = os.cpu_count()
+    Ts = 64
+    while True:
+        sd = dataclasses.replace(dims, T=Ts)
+        sub = dataclasses.replace(inp, dims=sd, logits=inp.logits[:Ts], x=inp.x[:Ts], dy=inp.dy[:Ts])
+        t0 = time.perf_counter()
+        ids, w = oracle.topk_softmax(sub.logits, sd.k)
+        oracle.route(ids, sd.E)
+        oracle.forward(sub, ids, w, sd, dtype=np.float32)
+        oracle.backward(sub, ids, w, sd, dtype=np.float32)
+        dt = time.perf_counter() - t0
+        if dt >= budget_s or Ts * 2 > dims.T:
+            break
+        Ts = min(dims.T, max(Ts * 2, int(Ts * budget_s / max(dt, 1e-3) * 0.9)))
+    return {"value": Ts / dt, "unit": "tokens/s", "cores": int(threads), "kind": "oracle",
+            "sample": f"first {Ts} of {dims.T} tokens, float32 numpy route+forward+backward, "
+                      f"one pass, {dt:.1f} s"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--config", default="qwen3_30b_a3b")
+    ap.add_argument("--cpu-budget", type=float, default=10.0,
+                    help="seconds of CPU oracle work for cpu_baseline (0 = skip)")
+    args = ap.parse_args()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}, WORLD_SIZE {world}); "
+              "this layer's data-parallel shards are independent and are not run here.",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import mixture_experts_lora_amd as mel
+    from mixture_experts_lora_amd import _lib
+    from synth import CONFIGS, make_inputs
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    mel.load()
+    c = CONFIGS[args.config]
+    inp = make_inputs(c, seed=0)
+    dims = mel.Dims(c.T, c.d, c.n, c.E, c.k, c.r, c.n_shared, c.lora_scale)
+
+    def bf(a):
+        return torch.from_numpy(a.view(np.int16)).cuda().view(torch.bfloat16)
+
+    w = mel.Weights(bf(inp.w_gu), bf(inp.w_dn), bf(inp.a_gu), bf(inp.b_gu), bf(inp.a_dn),
+                    bf(inp.b_dn))
+    logits = torch.from_numpy(inp.logits).cuda()
+    x, dy = bf(inp.x), bf(inp.dy)
+    layer = mel.MoELoRALayer(dims, w)
+
+    def step():
+        layer.route(logits)
+        layer.forward(x)
+        layer.backward(dy, x)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    t0 = torch.cuda.Event(enable_timing=True)
+    t1 = torch.cuda.Event(enable_timing=True)
+    t0.record()
+    for _ in range(args.steps):
+        step()
+    t1.record()
+    torch.cuda.synchronize()
+    ms = t0.elapsed_time(t1) / args.steps
+
+    # second timed region: the same steps with every kernel bracketed by events
+    _lib.timing_enable(True)
+    for _ in range(args.steps):
+        step()
+    torch.cuda.synchronize()
+    rep = _lib.timing_report()
+    _lib.timing_enable(False)
+    per_step = args.steps
+    work = kernel_work(c)
+    avg_us = {k: 1e3 * v[0] / v[1] for k, v in rep.items()}
+    gemm_flops = sum(work[k][0] for k in GEMM_KERNELS)
+    gemm_time = sum(rep[k][0] for k in GEMM_KERNELS if k in rep) / per_step * 1e-3
+    dom = "gate_up"
+    f, byts = work[dom]
+    t_dom = avg_us[dom] * 1e-6
+    hbm_bound = byts / PEAK_HBM >= f / PEAK_BF16
+    if hbm_bound:
+        roof = {"bound": "hbm", "achieved": byts / t_dom / 1e9, "peak": PEAK_HBM / 1e9,
+                "unit": "GB/s"}
+    else:
+        roof = {"bound": "mfma", "achieved": f / t_dom / 1e12, "peak": PEAK_BF16 / 1e12,
+                "unit": "TFLOP/s"}
+    roof["frac"] = roof["achieved"] / roof["peak"]
+    roof["traffic"] = None
+    roof["kernel"] = dom
+    roof["kernel_us"] = avg_us[dom]
+    roof["algorithmic_bytes"] = byts
+    roof["algorithmic_flops"] = f
+    roof["mfma_frac"] = f / t_dom / PEAK_BF16
+
+    out = {
+        "metric": METRIC,
+        "value": c.T / (ms * 1e-3),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded normal draws; no dataset, random-init weights)",
+        "config": {"workload": f"{c.name}: MoE-LoRA expert layer route+fwd+bwd", "T": c.T,
+                   "d": c.d, "n": c.n, "E": c.E, "top_k": c.k, "lora_rank": c.r,
+                   "n_shared": c.n_shared, "logits": c.logits_recipe},
+        "gemm_mfma_frac": gemm_flops / gemm_time / PEAK_BF16,
+        "gemm_tflops": gemm_flops / gemm_time / 1e12,
+        "roofline": roof,
+        "kernels_us": {k: round(v, 2) for k, v in sorted(avg_us.items())},
+    }
+    if args.cpu_budget > 0:
+        out["cpu_baseline"] = cpu_baseline(c, inp, args.cpu_budget)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

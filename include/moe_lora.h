@@ -1,0 +1,182 @@
+/*
+ * moe_lora.h -- C ABI of the MI355X (gfx950) MoE expert layer with split LoRA.
+ *
+ * The layer, as the two source pages describe it:
+ *
+ *  - Routing: the one-pass grouping from the article on Unsloth x NVIDIA
+ *    training optimisations (m.yhxrc.cn), section "Optimisation 3: MoE routing
+ *    grouped once": flatten every token's top-k expert assignments, sort them
+ *    stably by expert id, take all per-expert counts with one bincount, derive
+ *    offsets from the counts and slice the sorted list at those offsets.  The
+ *    per-expert search loop it replaces needs one data-dependent query per
+ *    expert; here nothing is ever read back to the host.
+ *
+ *  - Expert MLP: the Unsloth documentation page "Fine-tune MoE models 12x
+ *    faster with Unsloth".  Experts are stored as single stacked parameters
+ *    ("What is torch._grouped_mm?": gate_up [E, 2n, d], split into gate and up
+ *    halves after the projection); LoRA is kept split, i.e. X W^T + s (X A) B,
+ *    never merging B A^T into W ("Faster LoRA MoE training"; identical outputs
+ *    and gradients in exact arithmetic); an adapter on a weight of shape
+ *    (m, n) is A (m, r), B (r, n) ("Implementation details"); only A and B are
+ *    trained and the router stays frozen.
+ *
+ * Readings where the pages are silent: top-k ties go to the lower expert id;
+ * routing weights are the softmax of the k selected logits; offsets are
+ * exclusive with offsets[E] = T*k; gate is the first half of gate_up's rows;
+ * the activation is SwiGLU, h = silu(gate) * up; one optional shared expert is
+ * stacked as expert index E with weight 1 for every token.
+ *
+ * Conventions for every entry point
+ *  - All tensor pointers are DEVICE pointers (hipMalloc'd or torch CUDA
+ *    tensors), contiguous, row-major, 16-byte aligned.  bf16 tensors are passed
+ *    as raw 16-bit patterns (moe_bf16).
+ *  - The caller owns every buffer.  The library allocates no device memory,
+ *    frees nothing and keeps no pointer after returning; its only mutable
+ *    global state is the opt-in kernel-timing recorder declared at the end of
+ *    this file.  Calls on different streams are independent.
+ *  - Inputs are never written.  Outputs must not alias inputs or each other.
+ *  - Outputs are overwritten, never accumulated into (an expert that receives
+ *    no rows gets exactly zero LoRA gradients).
+ *  - Work is enqueued asynchronously on `stream` (a hipStream_t; NULL = the
+ *    default stream).  No call synchronises the host or copies to the host.
+ *  - The return code covers host-side validation and launch errors only; on
+ *    any error nothing has been enqueued except in the MOE_ERROR_LAUNCH case.
+ *  - Device-side data errors (an expert id outside [0, E) in a routing
+ *    struct that did not come from moe_route, non-finite logits) are not
+ *    detected; results are then undefined.
+ */
+#ifndef MOE_LORA_H
+#define MOE_LORA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef uint16_t moe_bf16; /* raw bf16 bits */
+
+typedef enum {
+  MOE_SUCCESS = 0,
+  MOE_ERROR_INVALID_VALUE = 1, /* null/misaligned pointer, T < 1, k not in [1,E], r < 1,
+                                  n_shared not in {0,1}, d or n < 1, non-finite lora_scale */
+  MOE_ERROR_UNSUPPORTED = 2,   /* outside the kernel envelope: d or n not a multiple of 64,
+                                  E > 256, r > 128, T*k + n_shared*T >= 2^31 */
+  MOE_ERROR_WORKSPACE = 3,     /* a workspace / saved buffer smaller than its size query */
+  MOE_ERROR_LAUNCH = 4         /* the HIP runtime reported an error when enqueueing */
+} moe_status;
+
+/* Layer shape.  T tokens, hidden size d, expert intermediate size n, E routed
+ * experts, top-k, LoRA rank r, n_shared shared experts (0 or 1, stacked after
+ * the routed ones), LoRA scale s applied to the low-rank term.
+ * Derived: P = T*k routed pairs; P_tot = P + n_shared*T rows of every grouped
+ * GEMM; E_tot = E + n_shared stacked experts. */
+typedef struct {
+  int64_t T;
+  int32_t d, n, E, k, r, n_shared;
+  float lora_scale;
+} moe_dims;
+
+/* Routing tensors, written by moe_route and read by forward/backward.
+ *   topk_ids    int32 [T, k]  expert ids per token, largest logit first
+ *   topk_w      fp32  [T, k]  softmax of the selected logits
+ *   counts      int32 [E]     rows per expert (one bincount)
+ *   offsets     int32 [E+1]   exclusive prefix sum of counts, offsets[E] = P
+ *   sorted_pair int32 [P]     flat pair index t*k + j at sorted position p;
+ *                             expert e owns positions [offsets[e], offsets[e+1]),
+ *                             ascending in t (stable)
+ *   pair_pos    int32 [P]     inverse permutation: sorted position of pair i */
+typedef struct {
+  int32_t* topk_ids;
+  float* topk_w;
+  int32_t* counts;
+  int32_t* offsets;
+  int32_t* sorted_pair;
+  int32_t* pair_pos;
+} moe_routing;
+
+/* Frozen base weights and LoRA factors, bf16, stacked over E_tot experts:
+ *   w_gate_up [E_tot, 2n, d]  rows [0,n) = gate, rows [n,2n) = up
+ *   w_down    [E_tot, d, n]
+ *   a_gate_up [E_tot, d, r]   b_gate_up [E_tot, r, 2n]
+ *   a_down    [E_tot, n, r]   b_down    [E_tot, r, d]
+ * The effective weights are W_gu + s (A_gu B_gu)^T and W_dn + s (A_dn B_dn)^T,
+ * but the library only ever forms (X A) B. */
+typedef struct {
+  const moe_bf16* w_gate_up;
+  const moe_bf16* w_down;
+  const moe_bf16* a_gate_up;
+  const moe_bf16* b_gate_up;
+  const moe_bf16* a_down;
+  const moe_bf16* b_down;
+} moe_weights;
+
+/* Human-readable name of a status code (static string, never NULL). */
+const char* moe_status_string(moe_status s);
+
+/* Size queries.  Each returns 0 if dims is NULL or invalid. */
+size_t moe_route_workspace_bytes(const moe_dims* dims);
+/* Buffer forward fills and backward reads: G [P_tot,2n], H [P_tot,n],
+ * X A_gu and H A_dn [P_tot, r] (all bf16). */
+size_t moe_forward_saved_bytes(const moe_dims* dims);
+/* Scratch for one forward or backward call (contents are not preserved). */
+size_t moe_workspace_bytes(const moe_dims* dims);
+
+/* Top-k softmax routing and the one-pass grouping (article section
+ * "Optimisation 3: MoE routing grouped once").
+ *   logits  fp32 [T, E] router logits (finite)
+ *   out     routing buffers to fill (all six pointers required)
+ *   ws      device scratch of at least moe_route_workspace_bytes(dims) */
+moe_status moe_route(const moe_dims* dims, const float* logits, const moe_routing* out,
+                     void* ws, size_t ws_bytes, void* stream);
+
+/* Forward of the expert layer with split LoRA (faster-MoE page, "What is
+ * torch._grouped_mm?" and "Faster LoRA MoE training"):
+ *   for each routed pair (t, j) with expert e = topk_ids[t,j]:
+ *     G = x_t W_gu[e]^T + s (x_t A_gu[e]) B_gu[e];  gate, up = G[:n], G[n:]
+ *     H = silu(gate) * up
+ *     O = H W_dn[e]^T + s (H A_dn[e]) B_dn[e]
+ *   y_t = sum_j topk_w[t,j] O(t,j)  (+ O of the shared expert, weight 1)
+ *   x     bf16 [T, d] hidden states
+ *   y     bf16 [T, d] output
+ *   saved buffer of moe_forward_saved_bytes(dims), kept unchanged for backward
+ *   ws    scratch of moe_workspace_bytes(dims) */
+moe_status moe_lora_forward(const moe_dims* dims, const moe_bf16* x, const moe_routing* routing,
+                            const moe_weights* weights, moe_bf16* y, void* saved,
+                            size_t saved_bytes, void* ws, size_t ws_bytes, void* stream);
+
+/* Backward for dX and the LoRA factors (the router and base weights are
+ * frozen, so no gradient is produced for them):
+ *   dy   bf16 [T, d] upstream gradient;  x as given to forward
+ *   saved  the buffer forward filled, with the same dims/routing/weights
+ *   dx   bf16 [T, d]
+ *   da_gate_up fp32 [E_tot, d, r]   db_gate_up fp32 [E_tot, r, 2n]
+ *   da_down    fp32 [E_tot, n, r]   db_down    fp32 [E_tot, r, d]
+ *   ws   scratch of moe_workspace_bytes(dims) */
+moe_status moe_lora_backward(const moe_dims* dims, const moe_bf16* dy, const moe_bf16* x,
+                             const moe_routing* routing, const moe_weights* weights,
+                             const void* saved, size_t saved_bytes, moe_bf16* dx,
+                             float* da_gate_up, float* db_gate_up, float* da_down,
+                             float* db_down, void* ws, size_t ws_bytes, void* stream);
+
+/* Kernel timing, for measurement tools (not part of the layer's math).
+ * moe_timing_enable(1) starts recording: every kernel the library enqueues
+ * afterwards is bracketed by two HIP events on its stream (a few
+ * microseconds of extra gaps per kernel).  moe_timing_enable(0) stops
+ * recording.  Both clear previous records.  Recording is process-wide and not
+ * thread-safe; the first enable creates the event pool (host call, no device
+ * memory).  Returns MOE_ERROR_LAUNCH if events cannot be created.
+ * moe_timing_report waits for the recorded events, then writes up to
+ * max_entries distinct kernel names (each NUL-terminated in a name_len-byte
+ * slot of `names`), the summed milliseconds and the launch count per name,
+ * clears the records and returns the number of entries (-1 on a HIP error).
+ * All buffers are host memory owned by the caller. */
+moe_status moe_timing_enable(int on);
+int moe_timing_report(char* names, int name_len, float* total_ms, int* launches, int max_entries);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MOE_LORA_H */

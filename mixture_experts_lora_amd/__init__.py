@@ -1,0 +1,23 @@
+"""MI355X (gfx950) MoE expert layer with split LoRA.
+
+The compute lives in the HIP library ``libmoe_lora.so`` (C ABI in
+``include/moe_lora.h``); this package only loads it and marshals torch
+tensors.  Importing the package does not load the library; the first call
+does, and fails loudly if it has not been built.
+"""
+from .api import (  # noqa: F401
+    Dims,
+    Grads,
+    MoELoRALayer,
+    Routing,
+    Weights,
+    backward,
+    empty_grads,
+    empty_routing,
+    forward,
+    forward_saved_bytes,
+    route,
+    route_workspace_bytes,
+    workspace_bytes,
+)
+from ._lib import MoeError, load  # noqa: F401

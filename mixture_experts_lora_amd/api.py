@@ -1,0 +1,248 @@
+"""torch-facing binding of the C ABI: allocation, checks and argument
+marshalling only.  Every step of routing, forward and backward runs in the
+HIP kernels of ``libmoe_lora.so``; nothing here computes."""
+from __future__ import annotations
+
+import ctypes
+from dataclasses import dataclass
+from typing import NamedTuple, Optional
+
+import torch
+
+from . import _lib
+
+
+@dataclass(frozen=True)
+class Dims:
+    """Layer shape (see moe_dims in include/moe_lora.h)."""
+
+    T: int
+    d: int
+    n: int
+    E: int
+    k: int
+    r: int
+    n_shared: int = 0
+    lora_scale: float = 1.0
+
+    @property
+    def P(self) -> int:
+        return self.T * self.k
+
+    @property
+    def P_tot(self) -> int:
+        return self.T * self.k + self.n_shared * self.T
+
+    @property
+    def E_tot(self) -> int:
+        return self.E + self.n_shared
+
+    def c(self) -> _lib.MoeDims:
+        return _lib.MoeDims(self.T, self.d, self.n, self.E, self.k, self.r, self.n_shared,
+                            float(self.lora_scale))
+
+
+class Routing(NamedTuple):
+    topk_ids: torch.Tensor     # int32 [T, k]
+    topk_w: torch.Tensor       # fp32  [T, k]
+    counts: torch.Tensor       # int32 [E]
+    offsets: torch.Tensor      # int32 [E+1]
+    sorted_pair: torch.Tensor  # int32 [P]
+    pair_pos: torch.Tensor     # int32 [P]
+
+
+class Weights(NamedTuple):
+    w_gate_up: torch.Tensor  # bf16 [E_tot, 2n, d]
+    w_down: torch.Tensor     # bf16 [E_tot, d, n]
+    a_gate_up: torch.Tensor  # bf16 [E_tot, d, r]
+    b_gate_up: torch.Tensor  # bf16 [E_tot, r, 2n]
+    a_down: torch.Tensor     # bf16 [E_tot, n, r]
+    b_down: torch.Tensor     # bf16 [E_tot, r, d]
+
+
+class Grads(NamedTuple):
+    dx: torch.Tensor          # bf16 [T, d]
+    da_gate_up: torch.Tensor  # fp32 [E_tot, d, r]
+    db_gate_up: torch.Tensor  # fp32 [E_tot, r, 2n]
+    da_down: torch.Tensor     # fp32 [E_tot, n, r]
+    db_down: torch.Tensor     # fp32 [E_tot, r, d]
+
+
+def _ptr(t: Optional[torch.Tensor]) -> Optional[int]:
+    return None if t is None else t.data_ptr()
+
+
+def _check(t: torch.Tensor, shape, dtype, name: str) -> None:
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name}: expected a torch.Tensor")
+    if not t.is_cuda:
+        raise ValueError(f"{name}: must be a GPU tensor")
+    if t.dtype != dtype:
+        raise ValueError(f"{name}: dtype {t.dtype}, expected {dtype}")
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name}: shape {tuple(t.shape)}, expected {tuple(shape)}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name}: must be contiguous")
+
+
+def _stream(stream) -> int:
+    s = torch.cuda.current_stream() if stream is None else stream
+    return s.cuda_stream
+
+
+def route_workspace_bytes(dims: Dims) -> int:
+    dc = dims.c()
+    return _lib.load().moe_route_workspace_bytes(ctypes.byref(dc))
+
+
+def forward_saved_bytes(dims: Dims) -> int:
+    dc = dims.c()
+    return _lib.load().moe_forward_saved_bytes(ctypes.byref(dc))
+
+
+def workspace_bytes(dims: Dims) -> int:
+    dc = dims.c()
+    return _lib.load().moe_workspace_bytes(ctypes.byref(dc))
+
+
+def _bytes(n: int, device) -> torch.Tensor:
+    return torch.empty(max(n, 16), dtype=torch.uint8, device=device)
+
+
+def empty_routing(dims: Dims, device) -> Routing:
+    i32 = torch.int32
+    return Routing(torch.empty(dims.T, dims.k, dtype=i32, device=device),
+                   torch.empty(dims.T, dims.k, dtype=torch.float32, device=device),
+                   torch.empty(dims.E, dtype=i32, device=device),
+                   torch.empty(dims.E + 1, dtype=i32, device=device),
+                   torch.empty(dims.P, dtype=i32, device=device),
+                   torch.empty(dims.P, dtype=i32, device=device))
+
+
+def _c_routing(rt: Routing) -> _lib.MoeRouting:
+    return _lib.MoeRouting(*[t.data_ptr() for t in rt])
+
+
+def _c_weights(w: Weights) -> _lib.MoeWeights:
+    return _lib.MoeWeights(*[t.data_ptr() for t in w])
+
+
+def _check_routing(rt: Routing, dims: Dims) -> None:
+    i32 = torch.int32
+    _check(rt.topk_ids, (dims.T, dims.k), i32, "topk_ids")
+    _check(rt.topk_w, (dims.T, dims.k), torch.float32, "topk_w")
+    _check(rt.counts, (dims.E,), i32, "counts")
+    _check(rt.offsets, (dims.E + 1,), i32, "offsets")
+    _check(rt.sorted_pair, (dims.P,), i32, "sorted_pair")
+    _check(rt.pair_pos, (dims.P,), i32, "pair_pos")
+
+
+def _check_weights(w: Weights, dims: Dims) -> None:
+    bf, Et, d, n, r = torch.bfloat16, dims.E_tot, dims.d, dims.n, dims.r
+    _check(w.w_gate_up, (Et, 2 * n, d), bf, "w_gate_up")
+    _check(w.w_down, (Et, d, n), bf, "w_down")
+    _check(w.a_gate_up, (Et, d, r), bf, "a_gate_up")
+    _check(w.b_gate_up, (Et, r, 2 * n), bf, "b_gate_up")
+    _check(w.a_down, (Et, n, r), bf, "a_down")
+    _check(w.b_down, (Et, r, d), bf, "b_down")
+
+
+def route(logits: torch.Tensor, dims: Dims, out: Optional[Routing] = None,
+          ws: Optional[torch.Tensor] = None, stream=None) -> Routing:
+    """moe_route: top-k softmax routing and the one-pass grouping."""
+    lib = _lib.load()
+    _check(logits, (dims.T, dims.E), torch.float32, "logits")
+    out = out if out is not None else empty_routing(dims, logits.device)
+    _check_routing(out, dims)
+    if ws is None:
+        ws = _bytes(route_workspace_bytes(dims), logits.device)
+    dc, rc = dims.c(), _c_routing(out)
+    _lib.check(lib.moe_route(ctypes.byref(dc), logits.data_ptr(), ctypes.byref(rc), ws.data_ptr(),
+                             ws.numel(), _stream(stream)), "moe_route")
+    return out
+
+
+def forward(x: torch.Tensor, routing: Routing, weights: Weights, dims: Dims,
+            y: Optional[torch.Tensor] = None, saved: Optional[torch.Tensor] = None,
+            ws: Optional[torch.Tensor] = None, stream=None):
+    """moe_lora_forward.  Returns (y, saved); keep `saved` for backward."""
+    lib = _lib.load()
+    _check(x, (dims.T, dims.d), torch.bfloat16, "x")
+    _check_routing(routing, dims)
+    _check_weights(weights, dims)
+    y = y if y is not None else torch.empty_like(x)
+    _check(y, (dims.T, dims.d), torch.bfloat16, "y")
+    if saved is None:
+        saved = _bytes(forward_saved_bytes(dims), x.device)
+    if ws is None:
+        ws = _bytes(workspace_bytes(dims), x.device)
+    dc, rc, wc = dims.c(), _c_routing(routing), _c_weights(weights)
+    _lib.check(lib.moe_lora_forward(ctypes.byref(dc), x.data_ptr(), ctypes.byref(rc),
+                                    ctypes.byref(wc), y.data_ptr(), saved.data_ptr(),
+                                    saved.numel(), ws.data_ptr(), ws.numel(), _stream(stream)),
+               "moe_lora_forward")
+    return y, saved
+
+
+def empty_grads(dims: Dims, device) -> Grads:
+    f32, Et, d, n, r = torch.float32, dims.E_tot, dims.d, dims.n, dims.r
+    return Grads(torch.empty(dims.T, d, dtype=torch.bfloat16, device=device),
+                 torch.empty(Et, d, r, dtype=f32, device=device),
+                 torch.empty(Et, r, 2 * n, dtype=f32, device=device),
+                 torch.empty(Et, n, r, dtype=f32, device=device),
+                 torch.empty(Et, r, d, dtype=f32, device=device))
+
+
+def backward(dy: torch.Tensor, x: torch.Tensor, routing: Routing, weights: Weights,
+             saved: torch.Tensor, dims: Dims, out: Optional[Grads] = None,
+             ws: Optional[torch.Tensor] = None, stream=None) -> Grads:
+    """moe_lora_backward: dX and the LoRA-factor gradients."""
+    lib = _lib.load()
+    _check(dy, (dims.T, dims.d), torch.bfloat16, "dy")
+    _check(x, (dims.T, dims.d), torch.bfloat16, "x")
+    _check_routing(routing, dims)
+    _check_weights(weights, dims)
+    out = out if out is not None else empty_grads(dims, dy.device)
+    Et, d, n, r = dims.E_tot, dims.d, dims.n, dims.r
+    _check(out.dx, (dims.T, d), torch.bfloat16, "dx")
+    _check(out.da_gate_up, (Et, d, r), torch.float32, "da_gate_up")
+    _check(out.db_gate_up, (Et, r, 2 * n), torch.float32, "db_gate_up")
+    _check(out.da_down, (Et, n, r), torch.float32, "da_down")
+    _check(out.db_down, (Et, r, d), torch.float32, "db_down")
+    if ws is None:
+        ws = _bytes(workspace_bytes(dims), dy.device)
+    dc, rc, wc = dims.c(), _c_routing(routing), _c_weights(weights)
+    _lib.check(lib.moe_lora_backward(ctypes.byref(dc), dy.data_ptr(), x.data_ptr(),
+                                     ctypes.byref(rc), ctypes.byref(wc), saved.data_ptr(),
+                                     saved.numel(), out.dx.data_ptr(), out.da_gate_up.data_ptr(),
+                                     out.db_gate_up.data_ptr(), out.da_down.data_ptr(),
+                                     out.db_down.data_ptr(), ws.data_ptr(), ws.numel(),
+                                     _stream(stream)),
+               "moe_lora_backward")
+    return out
+
+
+class MoELoRALayer:
+    """One layer with every buffer allocated up front, so that route / forward /
+    backward allocate nothing per call (the benchmark's steady state)."""
+
+    def __init__(self, dims: Dims, weights: Weights, device="cuda"):
+        _check_weights(weights, dims)
+        self.dims, self.weights = dims, weights
+        self.routing = empty_routing(dims, device)
+        self.route_ws = _bytes(route_workspace_bytes(dims), device)
+        self.saved = _bytes(forward_saved_bytes(dims), device)
+        self.ws = _bytes(workspace_bytes(dims), device)
+        self.y = torch.empty(dims.T, dims.d, dtype=torch.bfloat16, device=device)
+        self.grads = empty_grads(dims, device)
+
+    def route(self, logits, stream=None) -> Routing:
+        return route(logits, self.dims, self.routing, self.route_ws, stream)
+
+    def forward(self, x, stream=None) -> torch.Tensor:
+        forward(x, self.routing, self.weights, self.dims, self.y, self.saved, self.ws, stream)
+        return self.y
+
+    def backward(self, dy, x, stream=None) -> Grads:
+        return backward(dy, x, self.routing, self.weights, self.saved, self.dims, self.grads,
+                        self.ws, stream)

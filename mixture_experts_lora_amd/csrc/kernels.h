@@ -1,0 +1,98 @@
+// Internal interface between the C ABI (api.hip) and the kernel files.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace moe {
+
+typedef uint16_t bf16_t;
+
+// Everything one forward or backward call touches.  Device pointers only.
+// Rows of every grouped GEMM are "sorted positions" p in [0, P_tot): routed
+// pairs in expert order p < P (expert e owns [offsets[e], offsets[e+1])),
+// then the shared expert's T rows p = P + t.
+struct Layer {
+  int T, d, n, E, k, r, S, Et;
+  int rs;       // row stride of the rank-r activations (r rounded up to 8)
+  int ra;       // row stride used to read A_gu / A_dn (r, or rs for the packed copies)
+  int P, Ptot;  // routed pairs, all rows
+  float s;      // LoRA scale
+  int ncu;      // compute units of the device (persistent grid sizing)
+  // routing
+  const int32_t* topk_ids;
+  const float* topk_w;
+  const int32_t* offsets;
+  const int32_t* sorted_pair;
+  const int32_t* pair_pos;
+  // weights
+  const bf16_t* w_gu;  // [Et, 2n, d]
+  const bf16_t* w_dn;  // [Et, d, n]
+  const bf16_t* a_gu;  // [Et, d, ra]
+  const bf16_t* b_gu;  // [Et, r, 2n]
+  const bf16_t* a_dn;  // [Et, n, ra]
+  const bf16_t* b_dn;  // [Et, r, d]
+  // activations
+  const bf16_t* x;   // [T, d]
+  const bf16_t* dy;  // [T, d]
+  bf16_t* g;         // [Ptot, 2n]  saved
+  bf16_t* h;         // [Ptot, n]   saved
+  bf16_t* xa;        // [Ptot, rs]  saved
+  bf16_t* ha;        // [Ptot, rs]  saved
+  bf16_t* o;         // [Ptot, d]   forward: O; backward: dX per pair
+  bf16_t* dg;        // [Ptot, 2n]
+  bf16_t* qdn;       // [Ptot, rs]
+  bf16_t* qgu;       // [Ptot, rs]
+  bf16_t* y;         // [T, d]
+  bf16_t* dx;        // [T, d]
+  float* da_gu;      // [Et, d, r]
+  float* db_gu;      // [Et, r, 2n]
+  float* da_dn;      // [Et, n, r]
+  float* db_dn;      // [Et, r, d]
+  float* partial;    // split-K partial sums
+};
+
+// Workspace carving shared by the size query and the launchers.
+struct WsLayout {
+  size_t o, dg, qdn, qgu, partial, a_gu_pack, a_dn_pack, total;
+};
+struct SavedLayout {
+  size_t g, h, xa, ha, total;
+};
+WsLayout ws_layout(int64_t T, int d, int n, int E, int k, int r, int S);
+SavedLayout saved_layout(int64_t T, int d, int n, int E, int k, int r, int S);
+
+size_t route_ws_bytes(int64_t T, int E, int k);
+hipError_t launch_route(const float* logits, int64_t T, int E, int k, int32_t* ids, float* w,
+                        int32_t* counts, int32_t* offsets, int32_t* sorted_pair,
+                        int32_t* pair_pos, void* ws, hipStream_t st);
+
+// Grouped GEMM launchers (gemm.hip).
+hipError_t gemm_gate_up(const Layer& L, hipStream_t st);   // G, H  (+ X A_gu pre-pass)
+hipError_t gemm_down(const Layer& L, hipStream_t st);      // O     (+ H A_dn pre-pass)
+hipError_t gemm_dh(const Layer& L, hipStream_t st);        // dG    (+ dO B_dn^T pre-pass)
+hipError_t gemm_dx(const Layer& L, hipStream_t st);        // dX per pair (+ dG B_gu^T)
+hipError_t gemm_lora_grads(const Layer& L, hipStream_t st);  // dA, dB of both modules
+
+// Element-wise / gather kernels (layer.hip).
+hipError_t launch_pack_a(const Layer& L, const bf16_t* a_gu_src, const bf16_t* a_dn_src,
+                         bf16_t* a_gu_dst, bf16_t* a_dn_dst, hipStream_t st);
+hipError_t launch_combine(const Layer& L, bool weighted, const bf16_t* src, bf16_t* dst,
+                          hipStream_t st);
+
+int device_cu_count();
+
+// Kernel launch through the optional event-timing recorder (timing.hip).
+void timing_pre(const char* name, hipStream_t st);
+void timing_post(hipStream_t st);
+#define MOE_LAUNCH(name, kernel, grid, block, lds, stream, ...)              \
+  do {                                                                       \
+    ::moe::timing_pre(name, stream);                                         \
+    hipLaunchKernelGGL(kernel, grid, block, lds, stream, __VA_ARGS__);       \
+    ::moe::timing_post(stream);                                              \
+  } while (0)
+
+constexpr int SPLITK_ROWS = 2048;  // segment rows per split-K chunk of the LoRA grads
+
+}  // namespace moe

@@ -1,0 +1,131 @@
+// Gather-combine, LoRA-factor packing and buffer layouts.
+#include <atomic>
+
+#include <algorithm>
+
+#include "common.h"
+#include "kernels.h"
+
+namespace moe {
+
+static size_t align256(size_t v) { return (v + 255) & ~(size_t)255; }
+
+WsLayout ws_layout(int64_t T, int d, int n, int E, int k, int r, int S) {
+  const int64_t Ptot = T * k + (int64_t)S * T;
+  const int64_t Et = E + S;
+  const int64_t rs = (r + 7) / 8 * 8;
+  WsLayout w;
+  size_t off = 0;
+  w.o = off;        off += align256((size_t)Ptot * d * 2);
+  w.dg = off;       off += align256((size_t)Ptot * 2 * n * 2);
+  w.qdn = off;      off += align256((size_t)Ptot * rs * 2);
+  w.qgu = off;      off += align256((size_t)Ptot * rs * 2);
+  const int64_t slots = Ptot / SPLITK_ROWS + Et;
+  const int64_t mn = (int64_t)rs * (d > 2 * n ? d : 2 * n);
+  w.partial = off;  off += align256((size_t)(slots * mn * 4));
+  const bool pack = (r % 8) != 0;
+  w.a_gu_pack = off; off += pack ? align256((size_t)(Et * d * rs * 2)) : 0;
+  w.a_dn_pack = off; off += pack ? align256((size_t)(Et * n * rs * 2)) : 0;
+  w.total = off;
+  return w;
+}
+
+SavedLayout saved_layout(int64_t T, int d, int n, int E, int k, int r, int S) {
+  (void)d;
+  (void)E;
+  const int64_t Ptot = T * k + (int64_t)S * T;
+  const int64_t rs = (r + 7) / 8 * 8;
+  SavedLayout s;
+  size_t off = 0;
+  s.g = off;  off += align256((size_t)Ptot * 2 * n * 2);
+  s.h = off;  off += align256((size_t)Ptot * n * 2);
+  s.xa = off; off += align256((size_t)Ptot * rs * 2);
+  s.ha = off; off += align256((size_t)Ptot * rs * 2);
+  s.total = off;
+  return s;
+}
+
+int device_cu_count() {
+  static std::atomic<int> cache[64];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0) return 256;
+  if (dev < 64) {
+    int v = cache[dev].load(std::memory_order_relaxed);
+    if (v > 0) return v;
+  }
+  int cu = 0;
+  if (hipDeviceGetAttribute(&cu, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cu <= 0)
+    cu = 256;
+  if (dev < 64) cache[dev].store(cu, std::memory_order_relaxed);
+  return cu;
+}
+
+// [rows, r] -> [rows, rs] with zero padding, for ranks that are not a
+// multiple of 8 (16-byte vector loads need 8-element rows).
+__global__ void k_pack_rank(const bf16_t* __restrict__ src, bf16_t* __restrict__ dst, int64_t rows,
+                            int r, int rs) {
+  const int64_t total = rows * rs;
+  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < total;
+       i += (int64_t)gridDim.x * blockDim.x) {
+    const int64_t row = i / rs;
+    const int c = (int)(i - row * rs);
+    dst[i] = c < r ? src[row * r + c] : (bf16_t)0;
+  }
+}
+
+hipError_t launch_pack_a(const Layer& L, const bf16_t* a_gu_src, const bf16_t* a_dn_src,
+                         bf16_t* a_gu_dst, bf16_t* a_dn_dst, hipStream_t st) {
+  const int64_t rows_gu = (int64_t)L.Et * L.d, rows_dn = (int64_t)L.Et * L.n;
+  const int gb = (int)std::min<int64_t>(cdiv64(rows_gu * L.rs, 256), 4096);
+  const int gd = (int)std::min<int64_t>(cdiv64(rows_dn * L.rs, 256), 4096);
+  MOE_LAUNCH("pack_a", k_pack_rank, dim3(gb), dim3(256), 0, st, a_gu_src, a_gu_dst, rows_gu, L.r, L.rs);
+  MOE_LAUNCH("pack_a", k_pack_rank, dim3(gd), dim3(256), 0, st, a_dn_src, a_dn_dst, rows_dn, L.r, L.rs);
+  return hipGetLastError();
+}
+
+// dst[t] = sum_j w[t,j] * src[pair_pos[t*k+j]]  (+ src[P + t] for the shared
+// expert), fp32 sum in slot order; w = 1 when not weighted (the backward,
+// where the routing weight already entered through dO).
+__global__ __launch_bounds__(256) void k_combine(const Layer L, int weighted,
+                                                 const bf16_t* __restrict__ src,
+                                                 bf16_t* __restrict__ dst) {
+  const int t = blockIdx.x;
+  const int d = L.d, k = L.k;
+  for (int c = threadIdx.x * 8; c < d; c += 256 * 8) {
+    float acc[8];
+#pragma unroll
+    for (int q = 0; q < 8; ++q) acc[q] = 0.0f;
+    for (int j = 0; j < k; ++j) {
+      const int64_t i = (int64_t)t * k + j;
+      const int64_t p = L.pair_pos[i];
+      const float w = weighted ? L.topk_w[i] : 1.0f;
+      const uint4 v = *(const uint4*)(src + p * d + c);
+      const uint32_t u[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        acc[2 * q] += w * bf2f((bf16_t)(u[q] & 0xffffu));
+        acc[2 * q + 1] += w * bf2f((bf16_t)(u[q] >> 16));
+      }
+    }
+    if (L.S) {
+      const uint4 v = *(const uint4*)(src + ((int64_t)L.P + t) * d + c);
+      const uint32_t u[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        acc[2 * q] += bf2f((bf16_t)(u[q] & 0xffffu));
+        acc[2 * q + 1] += bf2f((bf16_t)(u[q] >> 16));
+      }
+    }
+    *(uint4*)(dst + (int64_t)t * d + c) =
+        make_uint4(pack2(acc[0], acc[1]), pack2(acc[2], acc[3]), pack2(acc[4], acc[5]),
+                   pack2(acc[6], acc[7]));
+  }
+}
+
+hipError_t launch_combine(const Layer& L, bool weighted, const bf16_t* src, bf16_t* dst,
+                          hipStream_t st) {
+  MOE_LAUNCH(weighted ? "combine_y" : "combine_dx", k_combine, dim3(L.T), dim3(256), 0, st, L, weighted ? 1 : 0, src, dst);
+  return hipGetLastError();
+}
+
+}  // namespace moe

@@ -1,0 +1,52 @@
+"""Helpers shared by the GPU parity tests: upload seeded inputs, call the HIP
+library through its binding, compare with the oracle."""
+from __future__ import annotations
+
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import mixture_experts_lora_amd as mel
+
+TOL = 2e-2  # max |gpu - ref| / max |ref| per tensor (bf16 inputs, fp32 accumulate)
+
+
+def require_gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    mel.load()  # the HIP library must be there: no fallback
+
+
+def announce(*parts):
+    print("[case]", *parts, flush=True)
+    sys.stdout.flush()
+
+
+def mdims(ld) -> mel.Dims:
+    return mel.Dims(ld.T, ld.d, ld.n, ld.E, ld.k, ld.r, ld.n_shared, ld.lora_scale)
+
+
+def bf16_tensor(bits: np.ndarray, dev="cuda") -> torch.Tensor:
+    return torch.from_numpy(bits.view(np.int16)).to(dev).view(torch.bfloat16)
+
+
+def to_numpy_f64(t: torch.Tensor) -> np.ndarray:
+    return t.float().cpu().numpy().astype(np.float64)
+
+
+def upload(inp, dev="cuda"):
+    w = mel.Weights(*(bf16_tensor(getattr(inp, k), dev) for k in
+                      ("w_gu", "w_dn", "a_gu", "b_gu", "a_dn", "b_dn")))
+    logits = torch.from_numpy(inp.logits).to(dev)
+    return logits, bf16_tensor(inp.x, dev), bf16_tensor(inp.dy, dev), w
+
+
+def relerr(got, ref) -> float:
+    got = np.asarray(got, np.float64)
+    ref = np.asarray(ref, np.float64)
+    scale = np.max(np.abs(ref))
+    if scale == 0:
+        return float(np.max(np.abs(got)))
+    return float(np.max(np.abs(got - ref)) / scale)

@@ -1,0 +1,118 @@
+"""The C-ABI library without a GPU: it loads, exports every entry point the
+header declares, answers size queries and rejects bad arguments on the host
+before anything is enqueued."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from mixture_experts_lora_amd import _lib
+from synth import CONFIGS
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "moe_lora.h")
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(_lib.LIB_PATH):
+        pytest.fail("libmoe_lora.so not built (python -m mixture_experts_lora_amd.build)")
+    return _lib.load()
+
+
+def _declared():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(moe_[a-z_]+)\s*\(", text)))
+
+
+def test_exports_every_declared_symbol(lib):
+    names = _declared()
+    assert set(names) == set(_lib.EXPORTED)
+    for name in names:
+        assert hasattr(lib, name), name
+
+
+def test_status_strings(lib):
+    for code, name in ((0, "MOE_SUCCESS"), (1, "MOE_ERROR_INVALID_VALUE"), (2, "MOE_ERROR_UNSUPPORTED"),
+                       (3, "MOE_ERROR_WORKSPACE"), (4, "MOE_ERROR_LAUNCH")):
+        assert lib.moe_status_string(code).decode() == name
+
+
+def _dims(**kw):
+    base = dict(T=256, d=128, n=64, E=8, k=2, r=4, n_shared=0, lora_scale=1.0)
+    base.update(kw)
+    return _lib.MoeDims(**base)
+
+
+@pytest.mark.parametrize("name", list(CONFIGS))
+def test_size_queries(lib, name):
+    c = CONFIGS[name]
+    dm = _dims(T=c.T, d=c.d, n=c.n, E=c.E, k=c.k, r=c.r, n_shared=c.n_shared)
+    rs = (c.r + 7) // 8 * 8
+    saved = lib.moe_forward_saved_bytes(ctypes.byref(dm))
+    assert saved >= c.P_tot * (2 * c.n + c.n + 2 * rs) * 2
+    ws = lib.moe_workspace_bytes(ctypes.byref(dm))
+    assert ws >= c.P_tot * (c.d + 2 * c.n + 2 * rs) * 2
+    assert lib.moe_route_workspace_bytes(ctypes.byref(dm)) >= c.P * 4
+
+
+BAD = [
+    (dict(k=0), 1), (dict(k=9), 1), (dict(T=0), 1), (dict(r=0), 1), (dict(n_shared=2), 1),
+    (dict(lora_scale=float("inf")), 1), (dict(lora_scale=float("nan")), 1),
+    (dict(d=96), 2), (dict(n=100), 2), (dict(E=300, k=2), 2), (dict(r=129), 2),
+    (dict(T=1 << 29, k=8), 2),
+]
+
+
+@pytest.mark.parametrize("kw,code", BAD)
+def test_invalid_dims_rejected_on_host(lib, kw, code):
+    dm = _dims(**kw)
+    assert lib.moe_workspace_bytes(ctypes.byref(dm)) == 0
+    assert lib.moe_forward_saved_bytes(ctypes.byref(dm)) == 0
+    fake = ctypes.c_void_p(4096)  # never dereferenced: validation fails first
+    rt = _lib.MoeRouting(*([4096] * 6))
+    assert lib.moe_route(ctypes.byref(dm), fake, ctypes.byref(rt), fake, 1 << 40, None) == code
+    w = _lib.MoeWeights(*([4096] * 6))
+    assert lib.moe_lora_forward(ctypes.byref(dm), fake, ctypes.byref(rt), ctypes.byref(w), fake,
+                                fake, 1 << 40, fake, 1 << 40, None) == code
+
+
+def test_null_misaligned_and_small_buffers_rejected(lib):
+    dm = _dims()
+    fake = 4096
+    rt = _lib.MoeRouting(*([fake] * 6))
+    w = _lib.MoeWeights(*([fake] * 6))
+    big = 1 << 40
+    # null dims
+    assert lib.moe_route(None, fake, ctypes.byref(rt), fake, big, None) == 1
+    # null / misaligned pointers
+    assert lib.moe_route(ctypes.byref(dm), None, ctypes.byref(rt), fake, big, None) == 1
+    assert lib.moe_route(ctypes.byref(dm), fake + 4, ctypes.byref(rt), fake, big, None) == 1
+    bad_rt = _lib.MoeRouting(fake, fake, fake, 0, fake, fake)
+    assert lib.moe_route(ctypes.byref(dm), fake, ctypes.byref(bad_rt), fake, big, None) == 1
+    bad_w = _lib.MoeWeights(fake, fake, fake + 2, fake, fake, fake)
+    assert lib.moe_lora_forward(ctypes.byref(dm), fake, ctypes.byref(rt), ctypes.byref(bad_w), fake,
+                                fake, big, fake, big, None) == 1
+    # workspace smaller than its query
+    need = lib.moe_route_workspace_bytes(ctypes.byref(dm))
+    assert lib.moe_route(ctypes.byref(dm), fake, ctypes.byref(rt), fake, need - 1, None) == 3
+    saved = lib.moe_forward_saved_bytes(ctypes.byref(dm))
+    ws = lib.moe_workspace_bytes(ctypes.byref(dm))
+    assert lib.moe_lora_forward(ctypes.byref(dm), fake, ctypes.byref(rt), ctypes.byref(w), fake,
+                                fake, saved - 1, fake, ws, None) == 3
+    assert lib.moe_lora_forward(ctypes.byref(dm), fake, ctypes.byref(rt), ctypes.byref(w), fake,
+                                fake, saved, fake, ws - 1, None) == 3
+    assert lib.moe_lora_backward(ctypes.byref(dm), fake, fake, ctypes.byref(rt), ctypes.byref(w),
+                                 fake, saved, fake, fake, fake, fake, fake, fake, ws - 1, None) == 3
+    assert lib.moe_lora_backward(ctypes.byref(dm), fake, fake, ctypes.byref(rt), ctypes.byref(w),
+                                 fake, saved, fake, fake, 0, fake, fake, fake, ws, None) == 1
+
+
+def test_python_binding_refuses_cpu_tensors():
+    import torch
+    import mixture_experts_lora_amd as mel
+    dims = mel.Dims(T=4, d=64, n=64, E=2, k=1, r=4)
+    with pytest.raises(ValueError):
+        mel.route(torch.zeros(4, 2), dims)

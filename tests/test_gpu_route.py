@@ -1,0 +1,70 @@
+"""Routing on the GPU against the oracle: top-k ids, counts, offsets,
+sorted_pair and pair_pos bit-exact; routing weights to fp32 rounding."""
+import numpy as np
+import pytest
+import torch
+
+import mixture_experts_lora_amd as mel
+import oracle
+from gpu_helpers import announce, mdims, require_gpu
+from synth import CONFIGS, LayerDims, make_logits
+
+pytestmark = pytest.mark.gpu
+
+
+def _run_and_compare(dims_l, logits_np):
+    require_gpu()
+    dims = mdims(dims_l)
+    logits = torch.from_numpy(logits_np).cuda()
+    out = mel.empty_routing(dims, "cuda")
+    for t in out:  # sentinels: every element must be written
+        t.fill_(-7)
+    rt = mel.route(logits, dims, out)
+    again = mel.route(logits, dims)
+    torch.cuda.synchronize()
+    ids, w = oracle.topk_softmax(logits_np, dims.k)
+    R = oracle.route(ids, dims.E)
+    np.testing.assert_array_equal(rt.topk_ids.cpu().numpy(), ids)
+    np.testing.assert_array_equal(rt.counts.cpu().numpy(), R.counts)
+    np.testing.assert_array_equal(rt.offsets.cpu().numpy(), R.offsets)
+    np.testing.assert_array_equal(rt.sorted_pair.cpu().numpy(), R.sorted_pair)
+    np.testing.assert_array_equal(rt.pair_pos.cpu().numpy(), R.pair_pos)
+    np.testing.assert_allclose(rt.topk_w.cpu().numpy(), w, rtol=2e-6, atol=1e-7)
+    for a, b in zip(rt, again):  # deterministic
+        assert torch.equal(a, b)
+
+
+@pytest.mark.parametrize("name", list(CONFIGS))
+def test_route_configs(name):
+    announce("route", name)
+    d = CONFIGS[name]
+    _run_and_compare(d, make_logits(d))
+
+
+EDGE = [
+    LayerDims(1, 64, 64, 5, 3, 4),        # one token
+    LayerDims(100, 64, 64, 1, 1, 4),      # one expert
+    LayerDims(65, 64, 64, 8, 8, 4),       # k = E, ragged last block
+    LayerDims(130, 64, 64, 16, 1, 4),     # k = 1
+    LayerDims(777, 64, 64, 256, 8, 4),    # widest E
+    LayerDims(64, 64, 64, 256, 256, 4),   # k = E = 256
+    LayerDims(1000, 64, 64, 37, 5, 4),    # E not a power of two
+]
+
+
+@pytest.mark.parametrize("dims", EDGE, ids=lambda d: f"T{d.T}E{d.E}k{d.k}")
+def test_route_edges(dims):
+    announce("route edge", dims)
+    _run_and_compare(dims, make_logits(dims, seed=5))
+
+
+def test_route_ties_and_one_hot_expert():
+    announce("route ties")
+    rng = np.random.default_rng(3)
+    L = rng.integers(-2, 3, size=(300, 12)).astype(np.float32)
+    L[::7] = 0.0  # whole rows tied
+    L[5] = -0.0
+    _run_and_compare(LayerDims(300, 64, 64, 12, 4, 4), L)
+    L2 = np.zeros((200, 6), np.float32)
+    L2[:, 4] = 3.0
+    _run_and_compare(LayerDims(200, 64, 64, 6, 2, 4), L2)
