@@ -62,7 +62,8 @@ typedef enum {
   MOE_ERROR_INVALID_VALUE = 1, /* null/misaligned pointer, T < 1, k not in [1,E], r < 1,
                                   n_shared not in {0,1}, d or n < 1, non-finite lora_scale */
   MOE_ERROR_UNSUPPORTED = 2,   /* outside the kernel envelope: d or n not a multiple of 64,
-                                  E > 256, r > 128, T*k + n_shared*T >= 2^31 */
+                                  E > 256, r > 128, T*k + n_shared*T >= 2^31,
+                                  T*d*2 or 2n*d*2 bytes >= 2^31 */
   MOE_ERROR_WORKSPACE = 3,     /* a workspace / saved buffer smaller than its size query */
   MOE_ERROR_LAUNCH = 4         /* the HIP runtime reported an error when enqueueing */
 } moe_status;
@@ -118,7 +119,8 @@ const char* moe_status_string(moe_status s);
 /* Size queries.  Each returns 0 if dims is NULL or invalid. */
 size_t moe_route_workspace_bytes(const moe_dims* dims);
 /* Buffer forward fills and backward reads: G [P_tot,2n], H [P_tot,n],
- * X A_gu and H A_dn [P_tot, r] (all bf16). */
+ * X A_gu and H A_dn [P_tot, r] (all bf16), and the token index and routing
+ * weight of every sorted row. */
 size_t moe_forward_saved_bytes(const moe_dims* dims);
 /* Scratch for one forward or backward call (contents are not preserved). */
 size_t moe_workspace_bytes(const moe_dims* dims);

@@ -50,21 +50,24 @@ def _compile(src: str, extra: list[str]) -> str:
     return obj
 
 
-def build(extra_flags: list[str] | None = None, verbose: bool = True) -> str:
+def build(extra_flags: list[str] | None = None, verbose: bool = True, out: str = LIB,
+          objdir: str = OBJ) -> str:
     """Compile every HIP source for gfx950 and link ``libmoe_lora.so``."""
     extra = list(extra_flags or [])
+    global OBJ
+    OBJ = objdir
     os.makedirs(OBJ, exist_ok=True)
     with cf.ThreadPoolExecutor(max_workers=len(SOURCES)) as ex:
         objs = list(ex.map(lambda s: _compile(s, extra), SOURCES))
-    tmp = LIB + ".tmp"
+    tmp = out + ".tmp"
     cmd = [_hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs, "-o", tmp]
     res = subprocess.run(cmd, capture_output=True, text=True)
     if res.returncode != 0:
         raise RuntimeError(f"link failed:\n{res.stdout}\n{res.stderr}")
-    os.replace(tmp, LIB)
+    os.replace(tmp, out)
     if verbose:
-        print(f"built {LIB}")
-    return LIB
+        print(f"built {out}")
+    return out
 
 
 if __name__ == "__main__":

@@ -20,6 +20,10 @@ moe_status check_dims(const moe_dims* dm) {
   if (dm->d % 64 || dm->n % 64 || dm->E > 256 || dm->r > 128) return MOE_ERROR_UNSUPPORTED;
   const int64_t ptot = dm->T * (int64_t)dm->k + (int64_t)dm->n_shared * dm->T;
   if (ptot >= ((int64_t)1 << 31)) return MOE_ERROR_UNSUPPORTED;
+  // 32-bit buffer offsets: a [T, d] activation and one expert's [2n, d] weight
+  // must each stay below 2 GiB
+  if (dm->T * (int64_t)dm->d * 2 >= ((int64_t)1 << 31)) return MOE_ERROR_UNSUPPORTED;
+  if ((int64_t)2 * dm->n * dm->d * 2 >= ((int64_t)1 << 31)) return MOE_ERROR_UNSUPPORTED;
   return MOE_SUCCESS;
 }
 
@@ -85,6 +89,8 @@ void attach_common(Layer& L, const moe_routing* rt, const moe_weights* w, const 
   L.qdn = (bf16_t*)(base + wl.qdn);
   L.qgu = (bf16_t*)(base + wl.qgu);
   L.partial = (float*)(base + wl.partial);
+  L.pre_partial = (float*)(base + wl.pre_partial);
+  for (int i = 0; i < 4; ++i) L.partial_off[i] = wl.partial_off[i];
 }
 
 void attach_saved(Layer& L, const moe_dims* dm, void* saved) {
@@ -94,6 +100,8 @@ void attach_saved(Layer& L, const moe_dims* dm, void* saved) {
   L.h = (bf16_t*)(base + sl.h);
   L.xa = (bf16_t*)(base + sl.xa);
   L.ha = (bf16_t*)(base + sl.ha);
+  L.tok = (const int32_t*)(base + sl.tok);
+  L.wgt = (const float*)(base + sl.wgt);
 }
 
 hipError_t maybe_pack(const Layer& L, const moe_weights* w, hipStream_t st) {
@@ -163,6 +171,7 @@ moe_status moe_lora_forward(const moe_dims* dm, const moe_bf16* x, const moe_rou
   L.x = x;
   L.y = y;
   hipError_t e = maybe_pack(L, w, s);
+  if (e == hipSuccess) e = launch_gather_table(L, (int32_t*)L.tok, (float*)L.wgt, s);
   if (e == hipSuccess) e = gemm_gate_up(L, s);
   if (e == hipSuccess) e = gemm_down(L, s);
   if (e == hipSuccess) e = launch_combine(L, true, L.o, L.y, s);

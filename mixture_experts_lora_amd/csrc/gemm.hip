@@ -4,7 +4,7 @@
 // segments of the sorted (token, expert) pairs, against that expert's slice of
 // a stacked parameter (Unsloth faster-MoE page, "What is torch._grouped_mm?").
 // The LoRA term stays split ("Faster LoRA MoE training"): the rank-r
-// activation (X A, H A_dn, dO B_dn^T, dG B_gu^T) is produced by a skinny
+// activation (X A_gu, H A_dn, dO B_dn^T, dG B_gu^T) comes from a skinny
 // pre-pass, and its product with the other factor runs as a second, short
 // MFMA pass into the SAME accumulator tile as the base product, so the
 // adapter delta (A B)^T is never formed.
@@ -14,8 +14,14 @@
 //  - v_mfma_f32_32x32x16_bf16, fp32 accumulation; the operands are swapped
 //    (mfma(B, A)) so each lane owns 4 consecutive output columns of one row
 //    and the epilogue writes 8-byte (bf16) or 16-byte (fp32) vectors;
+//  - operands come in through buffer loads (buffer_load_dwordx4): rows
+//    outside a segment and columns outside a matrix get a vector offset past
+//    the buffer's range and read as zero in hardware, so the K loop has no
+//    branches; for row-contiguous operands the K offset of a step is a scalar
+//    register that only moves inside a row already range-checked;
 //  - LDS holds both operands K-contiguous, rows padded to 72 elements, two
-//    stages (global loads of step k+1 are in flight during the MFMAs of k);
+//    stages; global loads run two K steps ahead of the MFMAs (two register
+//    stages);
 //  - operands whose contraction index is the row index in memory (the weights
 //    in the backward, the segment rows in the LoRA-gradient reductions) are
 //    loaded as 4(k) x 8(mn) blocks and transposed in registers before the
@@ -32,15 +38,23 @@
 
 namespace moe {
 
-constexpr int NT = 256;
+#ifndef MOE_PGR
+#define MOE_PGR 2
+#endif
+
 constexpr int BK = 64;
 constexpr int LDK = BK + 8;
 constexpr int MAX_ET = 512;
 
-template <int BM_, int BN_, int WM_, int WN_>
+// Tile configuration: BM x BN outputs per workgroup, WM x WN waves (64
+// threads each), PGR register stages of global prefetch (1 or 2).
+template <int BM_, int BN_, int WM_, int WN_, int PGR_ = MOE_PGR>
 struct Cfg {
-  static constexpr int BM = BM_, BN = BN_, WAVES_M = WM_, WAVES_N = WN_;
-  static_assert(WM_ * WN_ == 4, "four waves");
+  static constexpr int BM = BM_, BN = BN_, WAVES_M = WM_, WAVES_N = WN_, PGR = PGR_;
+  static constexpr int NW = WM_ * WN_, NT = 64 * NW;
+  // waves per SIMD the register allocation must allow: two workgroups of 4
+  // waves, or one of 8
+  static constexpr int OCC = 2;
   static constexpr int TM = BM / WM_, TN = BN / WN_;
   static constexpr int FM = TM / 32, FN = TN / 32;
   static_assert(FM >= 1 && FN >= 1, "wave tile at least 32x32");
@@ -49,6 +63,21 @@ struct Cfg {
   static constexpr int LDS_ELEMS = 2 * STAGE;
 };
 
+// ---------------------------------------------------------------- buffer loads
+
+typedef __amdgpu_buffer_rsrc_t rsrc_t;
+constexpr uint32_t OOB = 0x80000000u;  // offset past every buffer: reads as zero
+
+__device__ __forceinline__ rsrc_t make_rsrc(const void* base, int64_t bytes) {
+  const int64_t cap = 0x7fffffff;
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0,
+                                           (int)(bytes < cap ? bytes : cap), 0x00020000);
+}
+__device__ __forceinline__ uint4 bload16(rsrc_t r, uint32_t voff, uint32_t soff) {
+  const auto v = __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, 0);
+  return make_uint4(v[0], v[1], v[2], v[3]);
+}
+
 // ---------------------------------------------------------------- helpers
 
 __device__ __forceinline__ int seg_start(const Layer& L, int e) {
@@ -56,29 +85,6 @@ __device__ __forceinline__ int seg_start(const Layer& L, int e) {
 }
 __device__ __forceinline__ int seg_count(const Layer& L, int e) {
   return e < L.E ? L.offsets[e + 1] - L.offsets[e] : L.T;
-}
-__device__ __forceinline__ int token_of(const Layer& L, int p) {
-  return p < L.P ? L.sorted_pair[p] / L.k : p - L.P;
-}
-__device__ __forceinline__ float weight_of(const Layer& L, int p) {
-  return p < L.P ? L.topk_w[L.sorted_pair[p]] : 1.0f;
-}
-
-// sorted position -> token / routing weight, small enough to capture by value
-struct Rows {
-  const int32_t* sp;
-  const float* w;
-  int k, P;
-  __device__ __forceinline__ int token(int p) const { return p < P ? sp[p] / k : p - P; }
-  __device__ __forceinline__ float weight(int p) const { return p < P ? w[sp[p]] : 1.0f; }
-};
-__device__ __forceinline__ Rows rows_of(const Layer& L) {
-  Rows r;
-  r.sp = L.sorted_pair;
-  r.w = L.topk_w;
-  r.k = L.k;
-  r.P = L.P;
-  return r;
 }
 
 __device__ __forceinline__ uint32_t scale2(uint32_t w, float s) {
@@ -93,128 +99,189 @@ __device__ __forceinline__ uint32_t word_of(const uint4& v, int i) {
 
 // ---------------------------------------------------------------- operand panels
 
-// R rows of a K-contiguous source (row r at rowptr(r), K elements in a row);
-// each thread moves 16-byte chunks.
-template <int R, class RowFn>
-struct KOperand {
+// R rows of a K-contiguous source; row r starts at byte rowoff(r) of the
+// buffer (negative = a zero row).  Each thread moves 16-byte chunks; the K
+// offset of a step goes in the scalar offset.  KCHECK masks chunks at or past
+// kmax (narrow rank-r rows); SCALED multiplies each row by its own factor
+// (dO = w * dY); `cs` is a uniform factor (the LoRA scale), applied when != 1.
+template <int R, int NT, bool KCHECK, bool SCALED>
+struct KOp {
   static constexpr int CH = R * (BK / 8);
   static constexpr int PER = (CH + NT - 1) / NT;
-  const bf16_t* ptr[PER];
+  rsrc_t rs;
+  uint32_t voff[PER];
   float scl[PER];
-  uint4 v[PER];
+  uint4 v[2][PER];
   int kmax;
-  bool scaled;
+  float cs;
 
-  __device__ KOperand(RowFn rowfn, int kmax_, bool scaled_) : kmax(kmax_), scaled(scaled_) {
+  template <class RowFn>
+  __device__ KOp(rsrc_t r, RowFn rowoff, int kmax_, float cs_ = 1.0f) : rs(r), kmax(kmax_), cs(cs_) {
 #pragma unroll
     for (int i = 0; i < PER; ++i) {
       const int c = threadIdx.x + i * NT;
       float sc = 1.0f;
-      const bf16_t* p = nullptr;
-      if (c < CH) p = rowfn(c >> 3, sc);
-      ptr[i] = p ? p + (c & 7) * 8 : nullptr;
+      int64_t o = -1;
+      if (c < CH) o = rowoff(c >> 3, sc);
+      voff[i] = o < 0 ? OOB : (uint32_t)o + (uint32_t)((c & 7) * 16);
       scl[i] = sc;
     }
   }
+  template <int S>
   __device__ __forceinline__ void fetch(int k0) {
 #pragma unroll
     for (int i = 0; i < PER; ++i) {
-      const int c = threadIdx.x + i * NT;
-      if (ptr[i] && k0 + (c & 7) * 8 < kmax)
-        v[i] = *(const uint4*)(ptr[i] + k0);
-      else
-        v[i] = make_uint4(0, 0, 0, 0);
+      uint32_t o = voff[i];
+      if (KCHECK) {
+        const int c = threadIdx.x + i * NT;
+        if (k0 + (c & 7) * 8 >= kmax) o = OOB;
+      }
+      v[S][i] = bload16(rs, o, (uint32_t)k0 * 2u);
     }
   }
+  template <int S>
   __device__ __forceinline__ void store(bf16_t* lds) {
 #pragma unroll
     for (int i = 0; i < PER; ++i) {
       const int c = threadIdx.x + i * NT;
       if (CH % NT == 0 || c < CH) {
-        uint4 w = v[i];
-        if (scaled) w = scale8(w, scl[i]);
+        uint4 w = v[S][i];
+        if (SCALED) w = scale8(w, scl[i] * cs);
+        else if (cs != 1.0f) w = scale8(w, cs);
         *(uint4*)(lds + (c >> 3) * LDK + (c & 7) * 8) = w;
       }
     }
   }
 };
 
-// R columns of a source whose contraction index is the row index: element
-// (k, c) at krow(k)[col(c)], 8 consecutive columns contiguous.  A thread
-// loads a 4(k) x 8(c) block and writes it transposed into the K-contiguous
-// LDS panel.  Lane mapping (kq fastest) keeps a half-wave's 8-byte LDS stores
-// on distinct banks.
-template <int R, class KRowFn>
-struct MNOperand {
+// Transposing store shared by the MN panels: a thread's 4(k) x 8(c) block
+// goes to 8 LDS rows (one per column c) as 4 consecutive k values.  The lane
+// mapping (kq fastest) puts a half-wave's 8-byte stores on distinct banks.
+__device__ __forceinline__ void store_block_t(bf16_t* lds, int kq, int mg, const uint4 (&w)[4]) {
+#pragma unroll
+  for (int c = 0; c < 8; ++c) {
+    const int sh = (c & 1) * 16;
+    const uint32_t e0 = (word_of(w[0], c >> 1) >> sh) & 0xffffu;
+    const uint32_t e1 = (word_of(w[1], c >> 1) >> sh) & 0xffffu;
+    const uint32_t e2 = (word_of(w[2], c >> 1) >> sh) & 0xffffu;
+    const uint32_t e3 = (word_of(w[3], c >> 1) >> sh) & 0xffffu;
+    *(uint2*)(lds + (mg * 8 + c) * LDK + kq * 4) = make_uint2(e0 | (e1 << 16), e2 | (e3 << 16));
+  }
+}
+
+// R columns of a source whose contraction index is its row index: element
+// (k, c) at byte k*ldb + 2*col(c) of the buffer (the buffer starts at the
+// first row of the contraction range and ends with its last row, so rows past
+// the range read as zero).  8 consecutive columns are contiguous.
+template <int R, int NT>
+struct MNOp {
   static constexpr int NB = (BK / 4) * (R / 8);
   static constexpr int PER = (NB + NT - 1) / NT;
-  int col[PER];  // element offset of the block's first column, -1 = outside
-  uint4 v[PER][4];
-  float scl[PER][4];
-  KRowFn krow;
-  int kbase, kmax;
-  bool scaled;
+  rsrc_t rs;
+  uint32_t colb[PER];
+  uint32_t ldb;
+  float cs;
+  uint4 v[2][PER][4];
 
   template <class ColFn>
-  __device__ MNOperand(ColFn colfn, KRowFn krow_, int kbase_, int kmax_, bool scaled_)
-      : krow(krow_), kbase(kbase_), kmax(kmax_), scaled(scaled_) {
+  __device__ MNOp(rsrc_t r, ColFn colfn, uint32_t ldb_, float cs_ = 1.0f) : rs(r), ldb(ldb_), cs(cs_) {
 #pragma unroll
     for (int i = 0; i < PER; ++i) {
       const int bi = threadIdx.x + i * NT;
-      col[i] = bi < NB ? colfn((bi >> 4) * 8) : -1;
+      const int c = bi < NB ? colfn((bi >> 4) * 8) : -1;
+      colb[i] = c < 0 ? OOB : (uint32_t)c * 2u;
     }
   }
+  template <int S>
   __device__ __forceinline__ void fetch(int k0) {
 #pragma unroll
     for (int i = 0; i < PER; ++i) {
       const int kq = (threadIdx.x + i * NT) & 15;
 #pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const int kr = kbase + k0 + kq * 4 + q;
-        float sc = 1.0f;
-        const bf16_t* p = (col[i] >= 0 && kr < kmax) ? krow(kr, sc) : nullptr;
-        v[i][q] = p ? *(const uint4*)(p + col[i]) : make_uint4(0, 0, 0, 0);
-        scl[i][q] = sc;
-      }
+      for (int q = 0; q < 4; ++q)  // the row goes in the range-checked vector offset
+        v[S][i][q] = bload16(rs, colb[i] + (uint32_t)(k0 + kq * 4 + q) * ldb, 0);
     }
   }
+  template <int S>
   __device__ __forceinline__ void store(bf16_t* lds) {
 #pragma unroll
     for (int i = 0; i < PER; ++i) {
       const int bi = threadIdx.x + i * NT;
       if (NB % NT != 0 && bi >= NB) continue;
-      const int kq = bi & 15, mg = bi >> 4;
       uint4 w[4];
 #pragma unroll
-      for (int q = 0; q < 4; ++q) w[q] = scaled ? scale8(v[i][q], scl[i][q]) : v[i][q];
-#pragma unroll
-      for (int c = 0; c < 8; ++c) {
-        const int sh = (c & 1) * 16;
-        const uint32_t e0 = (word_of(w[0], c >> 1) >> sh) & 0xffffu;
-        const uint32_t e1 = (word_of(w[1], c >> 1) >> sh) & 0xffffu;
-        const uint32_t e2 = (word_of(w[2], c >> 1) >> sh) & 0xffffu;
-        const uint32_t e3 = (word_of(w[3], c >> 1) >> sh) & 0xffffu;
-        *(uint2*)(lds + (mg * 8 + c) * LDK + kq * 4) = make_uint2(e0 | (e1 << 16), e2 | (e3 << 16));
-      }
+      for (int q = 0; q < 4; ++q) w[q] = cs != 1.0f ? scale8(v[S][i][q], cs) : v[S][i][q];
+      store_block_t(lds, bi & 15, bi >> 4, w);
     }
   }
 };
 
-template <int R, class RowFn>
-__device__ __forceinline__ KOperand<R, RowFn> kop(RowFn f, int kmax, bool scaled = false) {
-  return KOperand<R, RowFn>(f, kmax, scaled);
-}
-template <int R, class ColFn, class KRowFn>
-__device__ __forceinline__ MNOperand<R, KRowFn> mnop(ColFn c, KRowFn f, int kbase, int kmax,
-                                                     bool scaled = false) {
-  return MNOperand<R, KRowFn>(c, f, kbase, kmax, scaled);
-}
+// As MNOp, but contraction row k is token tok[k] of a [T, ld] source (the
+// hidden states or the upstream gradient), optionally scaled by wgt[k].  The
+// gather indices of the next step are loaded one step ahead.
+template <int R, int NT, bool SCALED>
+struct MNGather {
+  static constexpr int NB = (BK / 4) * (R / 8);
+  static constexpr int PER = (NB + NT - 1) / NT;
+  rsrc_t rs, rtok, rwgt;
+  uint32_t colb[PER];
+  uint32_t ldb;
+  int kmax;
+  uint4 v[2][PER][4];
+  float scl[2][PER][4];
+  uint4 tn[PER], wn[PER];
+
+  template <class ColFn>
+  __device__ MNGather(rsrc_t r, rsrc_t rt, rsrc_t rw, ColFn colfn, uint32_t ldb_, int kmax_)
+      : rs(r), rtok(rt), rwgt(rw), ldb(ldb_), kmax(kmax_) {
+#pragma unroll
+    for (int i = 0; i < PER; ++i) {
+      const int bi = threadIdx.x + i * NT;
+      const int c = bi < NB ? colfn((bi >> 4) * 8) : -1;
+      colb[i] = c < 0 ? OOB : (uint32_t)c * 2u;
+      const uint32_t ro = (uint32_t)((bi & 15) * 4) * 4u;
+      tn[i] = bload16(rtok, ro, 0);
+      wn[i] = SCALED ? bload16(rwgt, ro, 0) : make_uint4(0, 0, 0, 0);
+    }
+  }
+  template <int S>
+  __device__ __forceinline__ void fetch(int k0) {
+#pragma unroll
+    for (int i = 0; i < PER; ++i) {
+      const int kq = (threadIdx.x + i * NT) & 15;
+      const uint4 t = tn[i], w = wn[i];
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const uint32_t tq = word_of(t, q);
+        const uint32_t o = (k0 + kq * 4 + q < kmax) ? colb[i] + tq * ldb : OOB;
+        v[S][i][q] = bload16(rs, o, 0);
+        scl[S][i][q] = SCALED ? __uint_as_float(word_of(w, q)) : 1.0f;
+      }
+      const uint32_t ro = (uint32_t)(k0 + BK + kq * 4) * 4u;
+      tn[i] = bload16(rtok, ro, 0);
+      if (SCALED) wn[i] = bload16(rwgt, ro, 0);
+    }
+  }
+  template <int S>
+  __device__ __forceinline__ void store(bf16_t* lds) {
+#pragma unroll
+    for (int i = 0; i < PER; ++i) {
+      const int bi = threadIdx.x + i * NT;
+      if (NB % NT != 0 && bi >= NB) continue;
+      uint4 w[4];
+#pragma unroll
+      for (int q = 0; q < 4; ++q) w[q] = SCALED ? scale8(v[S][i][q], scl[S][i][q]) : v[S][i][q];
+      store_block_t(lds, bi & 15, bi >> 4, w);
+    }
+  }
+};
 
 // ---------------------------------------------------------------- MFMA main loop
 
 template <class C>
 __device__ __forceinline__ void mma_stage(const bf16_t* As, const bf16_t* Bs,
-                                          f32x16 (&acc)[C::FM][C::FN]) {
+                                          f32x16 (&acc)[C::FM][C::FN], bool active) {
+  if (!active) return;  // the wave's rows or columns are all padding
   const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
   const int wm = wid / C::WAVES_N, wn = wid % C::WAVES_N;
   const bf16_t* ab = As + (wm * C::TM + (lane & 31)) * LDK + (lane >> 5) * 8;
@@ -233,31 +300,70 @@ __device__ __forceinline__ void mma_stage(const bf16_t* As, const bf16_t* Bs,
   }
 }
 
-// Pipelined K loop over nk steps of 64 (ends with a barrier, so the LDS can
-// be reused right after).
+// Pipelined K loop over nk steps of 64.  Global loads run MOE_PGR steps ahead
+// of the MFMAs, LDS is double-buffered, one barrier per step.  Ends with a
+// barrier, so the LDS can be reused right after.
 template <class C, class OA, class OB>
 __device__ __forceinline__ void run_loop(bf16_t* lds, OA& oa, OB& ob, int nk,
-                                         f32x16 (&acc)[C::FM][C::FN]) {
+                                         f32x16 (&acc)[C::FM][C::FN], bool active = true) {
   if (nk <= 0) return;
-  oa.fetch(0);
-  ob.fetch(0);
-  oa.store(lds);
-  ob.store(lds + C::A_ELEMS);
+  if constexpr (C::PGR == 1) {
+  oa.template fetch<0>(0);
+  ob.template fetch<0>(0);
+  oa.template store<0>(lds);
+  ob.template store<0>(lds + C::A_ELEMS);
   __syncthreads();
   for (int kt = 0; kt < nk; ++kt) {
-    const bf16_t* As = lds + (kt & 1) * C::STAGE;
-    const bool more = kt + 1 < nk;
-    if (more) {
-      oa.fetch((kt + 1) * BK);
-      ob.fetch((kt + 1) * BK);
+    bf16_t* cur = lds + (kt & 1) * C::STAGE;
+    bf16_t* nxt = lds + ((kt + 1) & 1) * C::STAGE;
+    if (kt + 1 < nk) {
+      oa.template fetch<0>((kt + 1) * BK);
+      ob.template fetch<0>((kt + 1) * BK);
     }
-    mma_stage<C>(As, As + C::A_ELEMS, acc);
-    if (more) {
-      bf16_t* An = lds + ((kt + 1) & 1) * C::STAGE;
-      oa.store(An);
-      ob.store(An + C::A_ELEMS);
+    mma_stage<C>(cur, cur + C::A_ELEMS, acc, active);
+    if (kt + 1 < nk) {
+      oa.template store<0>(nxt);
+      ob.template store<0>(nxt + C::A_ELEMS);
     }
     __syncthreads();
+  }
+  } else {
+  // Look-ahead fetches are issued unconditionally (past the last step they
+  // re-read the last step's addresses and are never stored), so the compiler
+  // can count outstanding loads exactly and waits only for the stage it needs.
+  const int klast = (nk - 1) * BK;
+  oa.template fetch<0>(0);
+  ob.template fetch<0>(0);
+  oa.template fetch<1>(min(BK, klast));
+  ob.template fetch<1>(min(BK, klast));
+  oa.template store<0>(lds);
+  ob.template store<0>(lds + C::A_ELEMS);
+  __syncthreads();
+  for (int kt = 0; kt < nk; kt += 2) {
+    {  // step kt: buffer 0; register stage 1 holds kt+1
+      bf16_t* nxt = lds + C::STAGE;
+      oa.template fetch<0>(min((kt + 2) * BK, klast));
+      ob.template fetch<0>(min((kt + 2) * BK, klast));
+      mma_stage<C>(lds, lds + C::A_ELEMS, acc, active);
+      if (kt + 1 < nk) {
+        oa.template store<1>(nxt);
+        ob.template store<1>(nxt + C::A_ELEMS);
+      }
+      __syncthreads();
+    }
+    if (kt + 1 >= nk) break;
+    {  // step kt+1: buffer 1; register stage 0 holds kt+2
+      bf16_t* cur = lds + C::STAGE;
+      oa.template fetch<1>(min((kt + 3) * BK, klast));
+      ob.template fetch<1>(min((kt + 3) * BK, klast));
+      mma_stage<C>(cur, cur + C::A_ELEMS, acc, active);
+      if (kt + 2 < nk) {
+        oa.template store<0>(lds);
+        ob.template store<0>(lds + C::A_ELEMS);
+      }
+      __syncthreads();
+    }
+  }
   }
 }
 
@@ -284,7 +390,7 @@ __device__ __forceinline__ void for_each_quad(f32x16 (&acc)[C::FM][C::FN], F f) 
       for (int g = 0; g < 4; ++g) {
         const int row = wm * C::TM + fm * 32 + (lane & 31);
         const int col = wn * C::TN + fn * 32 + g * 8 + (lane >> 5) * 4;
-        f(row, col, fn, acc[fm][fn][4 * g], acc[fm][fn][4 * g + 1], acc[fm][fn][4 * g + 2],
+        f(row, col, acc[fm][fn][4 * g], acc[fm][fn][4 * g + 1], acc[fm][fn][4 * g + 2],
           acc[fm][fn][4 * g + 3]);
       }
 }
@@ -302,295 +408,343 @@ __device__ __forceinline__ int first_tile() {
   return (G & 7) ? (int)blockIdx.x : (int)((blockIdx.x & 7) * (G >> 3) + (blockIdx.x >> 3));
 }
 
-// Row-ragged schedule: tiles (e, nt, mt), mt fastest; BM rows of a segment.
-struct MSched {
-  int* pre;  // [Et+1] exclusive prefix of per-expert M-tile counts
-  int Et;
-  template <int BM>
-  __device__ void init(const Layer& L, int* lds_pre, int* sh) {
-    pre = lds_pre;
-    Et = L.Et;
-    const int e0 = 2 * threadIdx.x, e1 = e0 + 1;
-    const int c0 = e0 < Et ? cdiv(seg_count(L, e0), BM) : 0;
-    const int c1 = e1 < Et ? cdiv(seg_count(L, e1), BM) : 0;
-    int tot;
-    const int ex = block_excl_scan256(c0 + c1, sh, &tot);
-    if (e0 < Et) pre[e0] = ex;
-    if (e1 < Et) pre[e1] = ex + c0;
-    if (threadIdx.x == 0) pre[Et] = tot;
-    __syncthreads();
+// Exclusive scan of one int per thread over a block of NW waves (all threads
+// must call); `sh` holds NW ints.
+template <int NW>
+__device__ __forceinline__ int block_excl_scan(int v, int* sh, int* total) {
+  const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
+  int x = v;
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const int y = __shfl_up(x, off, 64);
+    if (lane >= off) x += y;
   }
-  __device__ int total_m() const { return pre[Et]; }
-  __device__ void decode(int t, int ntn, int& e, int& mt, int& nt) const {
-    int lo = 0, hi = Et - 1;  // largest e with pre[e]*ntn <= t
-    while (lo < hi) {
-      const int mid = (lo + hi + 1) >> 1;
-      if (pre[mid] * ntn <= t) lo = mid; else hi = mid - 1;
-    }
-    e = lo;
-    const int local = t - pre[e] * ntn;
-    const int nm = pre[e + 1] - pre[e];
-    nt = local / nm;
-    mt = local - nt * nm;
+  if (lane == 63) sh[wid] = x;
+  __syncthreads();
+  int base = 0, tot = 0;
+#pragma unroll
+  for (int w = 0; w < NW; ++w) {
+    const int t = sh[w];
+    if (w < wid) base += t;
+    tot += t;
   }
-};
+  __syncthreads();
+  *total = tot;
+  return base + x - v;
+}
 
-// Contraction-ragged schedule (LoRA gradients): per expert, the segment rows
-// are split in chunks of SPLITK_ROWS; tiles (slot, nt, mt) with slot =
-// pre[e] + chunk.
-struct KSched {
-  int* pre;
-  int Et;
-  __device__ void init(const Layer& L, int* lds_pre, int* sh) {
-    pre = lds_pre;
-    Et = L.Et;
-    const int e0 = 2 * threadIdx.x, e1 = e0 + 1;
-    const int c0 = e0 < Et ? cdiv(seg_count(L, e0), SPLITK_ROWS) : 0;
-    const int c1 = e1 < Et ? cdiv(seg_count(L, e1), SPLITK_ROWS) : 0;
-    int tot;
-    const int ex = block_excl_scan256(c0 + c1, sh, &tot);
-    if (e0 < Et) pre[e0] = ex;
-    if (e1 < Et) pre[e1] = ex + c0;
-    if (threadIdx.x == 0) pre[Et] = tot;
-    __syncthreads();
+// Per-expert counts of a schedule unit (M tiles, or split-K chunks) and their
+// exclusive prefix over experts, in LDS.  Each thread takes EP consecutive
+// experts.
+template <int NT, class CountFn>
+__device__ __forceinline__ void expert_prefix(const Layer& L, int* pre, int* sh, CountFn cnt) {
+  constexpr int EP = (MAX_ET + NT - 1) / NT;
+  const int Et = L.Et;
+  int c[EP], sum = 0;
+#pragma unroll
+  for (int i = 0; i < EP; ++i) {
+    const int e = EP * threadIdx.x + i;
+    c[i] = e < Et ? cnt(e) : 0;
+    sum += c[i];
   }
-  __device__ int slots() const { return pre[Et]; }
-  __device__ int expert_of_slot(int slot) const {
-    int lo = 0, hi = Et - 1;
-    while (lo < hi) {
-      const int mid = (lo + hi + 1) >> 1;
-      if (pre[mid] <= slot) lo = mid; else hi = mid - 1;
-    }
-    return lo;
+  int tot;
+  int ex = block_excl_scan<NT / 64>(sum, sh, &tot);
+#pragma unroll
+  for (int i = 0; i < EP; ++i) {
+    const int e = EP * threadIdx.x + i;
+    if (e < Et) pre[e] = ex;
+    ex += c[i];
   }
+  if (threadIdx.x == 0) pre[Et] = tot;
+  __syncthreads();
+}
+
+// largest e in [0, Et) with pre[e] * mul <= t
+__device__ __forceinline__ int find_expert(const int* pre, int Et, int t, int mul) {
+  int lo = 0, hi = Et - 1;
+  while (lo < hi) {
+    const int mid = (lo + hi + 1) >> 1;
+    if (pre[mid] * mul <= t) lo = mid; else hi = mid - 1;
+  }
+  return lo;
+}
+
+// Row-ragged tile (e, nt, mt), mt fastest.
+struct MTile {
+  int e, mt, nt, row0, mrows;
 };
+template <int BM>
+__device__ __forceinline__ MTile decode_m(const Layer& L, const int* pre, int t, int ntn) {
+  MTile T;
+  T.e = find_expert(pre, L.Et, t, ntn);
+  const int local = t - pre[T.e] * ntn;
+  const int nm = pre[T.e + 1] - pre[T.e];
+  T.nt = local / nm;
+  T.mt = local - T.nt * nm;
+  T.row0 = seg_start(L, T.e) + T.mt * BM;
+  T.mrows = min(BM, seg_count(L, T.e) - T.mt * BM);
+  return T;
+}
 
 // ---------------------------------------------------------------- forward
 
 // gate/up column interleave of the gate_up tile: 32-column groups alternate
 // gate (rows j of W_gu) and up (rows n + j), so one lane holds gate and up of
-// the same (row, j) in its two N fragments.
+// the same (row, j) in two neighbouring N fragments.
 __device__ __forceinline__ int gu_row(int n, int j0, int c) {
   const int grp = c >> 5;
   return ((grp & 1) ? n : 0) + j0 + (grp >> 1) * 32 + (c & 31);
 }
 
-using CfgMain = Cfg<128, 128, 2, 2>;
+// Main-tile configurations (BM x BN, waves, prefetch depth); each of the four
+// main GEMMs picks one at compile time.
+template <int I> struct MainCfg;
+template <> struct MainCfg<0> { using type = Cfg<128, 128, 2, 2, 2>; };  // 4 waves of 64x64
+template <> struct MainCfg<1> { using type = Cfg<128, 256, 2, 4, 1>; };  // 8 waves of 64x64
+template <> struct MainCfg<2> { using type = Cfg<256, 128, 4, 2, 1>; };  // 8 waves of 64x64
+template <> struct MainCfg<3> { using type = Cfg<256, 256, 4, 2, 1>; };  // 8 waves of 64x128
+template <> struct MainCfg<4> { using type = Cfg<128, 256, 2, 2, 1>; };  // 4 waves of 64x128
+template <> struct MainCfg<5> { using type = Cfg<128, 128, 2, 2, 1>; };  // 4 waves of 64x64
+template <> struct MainCfg<6> { using type = Cfg<256, 128, 4, 2, 2>; };  // 8 waves of 64x64
+template <> struct MainCfg<7> { using type = Cfg<128, 256, 2, 4, 2>; };  // 8 waves of 64x64
+#ifndef MOE_CFG_GU
+#define MOE_CFG_GU 7
+#endif
+#ifndef MOE_CFG_DN
+#define MOE_CFG_DN 3
+#endif
+#ifndef MOE_CFG_DH
+#define MOE_CFG_DH 7
+#endif
+#ifndef MOE_CFG_DX
+#define MOE_CFG_DX 3
+#endif
+// Rank-r pre-passes: 128 rows x (64 | 128) rank columns, 4 waves.
+template <int BN>
+using CfgSkinny = Cfg<128, BN, 4, 1>;
 
-// G = X W_gu^T + s (X A_gu) B_gu ; H = silu(gate) * up.   Tile: 128 rows x 64 j.
-__global__ __launch_bounds__(NT) void k_gate_up(const Layer L) {
-  using C = CfgMain;
-  __shared__ __attribute__((aligned(16))) bf16_t lds[C::LDS_ELEMS];
-  __shared__ int pre[MAX_ET + 1];
-  __shared__ int sh[4];
-  MSched sch;
-  sch.init<C::BM>(L, pre, sh);
-  const int ntn = L.n / 64;
-  const int total = sch.total_m() * ntn;
-  const int n = L.n, d = L.d;
+#define MOE_GEMM_PROLOGUE(C)                                        \
+  __shared__ __attribute__((aligned(16))) bf16_t lds[C::LDS_ELEMS]; \
+  __shared__ int pre[MAX_ET + 1];                                   \
+  __shared__ int sh[C::NW];                                         \
+  expert_prefix<C::NT>(L, pre, sh, [&](int e) { return cdiv(seg_count(L, e), C::BM); });
+
+// true when this wave's rows [wm*TM, ..) start inside the tile's valid rows
+// and its columns start inside the valid columns
+template <class C>
+__device__ __forceinline__ bool wave_active(int mrows, int ncols) {
+  const int wid = threadIdx.x >> 6;
+  return (wid / C::WAVES_N) * C::TM < mrows && (wid % C::WAVES_N) * C::TN < ncols;
+}
+
+// G = X W_gu^T + s (X A_gu) B_gu ; H = silu(gate) * up.   Tile: BM rows x BN/2 j.
+template <class C>
+__global__ __launch_bounds__(C::NT) __attribute__((amdgpu_waves_per_eu(C::OCC))) void k_gate_up(const Layer L) {
+  MOE_GEMM_PROLOGUE(C)
+  constexpr int JT = C::BN / 2;
+  const int n = L.n, d = L.d, r = L.r, rs = L.rs;
+  const int ntn = cdiv(n, JT);
+  const int total = pre[L.Et] * ntn;
+  const rsrc_t rx = make_rsrc(L.x, (int64_t)L.T * d * 2);
   for (int t = first_tile(); t < total; t += gridDim.x) {
-    int e, mt, nt;
-    sch.decode(t, ntn, e, mt, nt);
-    const int row0 = seg_start(L, e) + mt * C::BM;
-    const int mrows = min(C::BM, seg_count(L, e) - mt * C::BM);
-    const int j0 = nt * 64;
+    const MTile T = decode_m<C::BM>(L, pre, t, ntn);
+    const int j0 = T.nt * JT;
+    const bool act = wave_active<C>(T.mrows, 2 * (n - j0));
     f32x16 acc[C::FM][C::FN];
     zero_acc<C>(acc);
     {
-      auto A = kop<C::BM>(
-          [&](int m, float&) -> const bf16_t* {
-            return m < mrows ? L.x + (int64_t)token_of(L, row0 + m) * d : nullptr;
+      const int32_t* tok = L.tok + T.row0;
+      const int mrows = T.mrows;
+      KOp<C::BM, C::NT, false, false> A(
+          rx, [&](int m, float&) -> int64_t { return m < mrows ? (int64_t)tok[m] * d * 2 : -1; }, d);
+      KOp<C::BN, C::NT, false, false> B(
+          make_rsrc(L.w_gu + (int64_t)T.e * 2 * n * d, (int64_t)2 * n * d * 2),
+          [&](int c, float&) -> int64_t {
+            const int row = gu_row(n, j0, c);
+            return (row % n) < n && j0 + (c >> 6) * 32 + (c & 31) < n ? (int64_t)row * d * 2 : -1;
           },
           d);
-      const bf16_t* wb = L.w_gu + (int64_t)e * 2 * n * d;
-      auto B = kop<C::BN>(
-          [&](int c, float&) -> const bf16_t* { return wb + (int64_t)gu_row(n, j0, c) * d; }, d);
-      run_loop<C>(lds, A, B, d / BK, acc);
+      run_loop<C>(lds, A, B, d / BK, acc, act);
     }
     {
-      auto A = kop<C::BM>(
-          [&](int m, float&) -> const bf16_t* {
-            return m < mrows ? L.xa + (int64_t)(row0 + m) * L.rs : nullptr;
-          },
-          L.rs);
-      const bf16_t* bb = L.b_gu + (int64_t)e * L.r * 2 * n;
-      const float s = L.s;
-      auto B = mnop<C::BN>([&](int c) { return gu_row(n, j0, c); },
-                           [=](int kr, float& sc) -> const bf16_t* {
-                             sc = s;
-                             return bb + (int64_t)kr * 2 * n;
+      KOp<C::BM, C::NT, true, false> A(make_rsrc(L.xa + (int64_t)T.row0 * rs, (int64_t)T.mrows * rs * 2),
+                                       [&](int m, float&) -> int64_t { return (int64_t)m * rs * 2; }, rs);
+      MNOp<C::BN, C::NT> B(make_rsrc(L.b_gu + (int64_t)T.e * r * 2 * n, (int64_t)r * 2 * n * 2),
+                           [&](int c) {
+                             return j0 + (c >> 6) * 32 + (c & 31) < n ? gu_row(n, j0, c) : -1;
                            },
-                           0, L.r, s != 1.0f);
-      run_loop<C>(lds, A, B, cdiv(L.rs, BK), acc);
+                           2 * n * 2, L.s);
+      run_loop<C>(lds, A, B, cdiv(rs, BK), acc, act);
     }
-    // SwiGLU epilogue: the lane's fragments fn=0 (gate) and fn=1 (up) cover the
+    // SwiGLU epilogue: a lane's fragments 2p (gate) and 2p+1 (up) cover the
     // same 32 j values.
-    {
-      const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
-      const int wm = wid / C::WAVES_N, wn = wid % C::WAVES_N;
+    const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
+    const int wm = wid / C::WAVES_N, wn = wid % C::WAVES_N;
 #pragma unroll
-      for (int fm = 0; fm < C::FM; ++fm) {
-        const int m = wm * C::TM + fm * 32 + (lane & 31);
-        if (m >= mrows) continue;
-        const int64_t p = row0 + m;
-        bf16_t* gr = L.g + p * 2 * n;
-        bf16_t* hr = L.h + p * n;
+    for (int fm = 0; fm < C::FM; ++fm) {
+      const int m = wm * C::TM + fm * 32 + (lane & 31);
+      if (m >= T.mrows) continue;
+      const int64_t p = T.row0 + m;
+      bf16_t* gr = L.g + p * 2 * n;
+      bf16_t* hr = L.h + p * n;
+#pragma unroll
+      for (int pr = 0; pr < C::FN / 2; ++pr) {
 #pragma unroll
         for (int g = 0; g < 4; ++g) {
-          const int j = j0 + wn * 32 + g * 8 + (lane >> 5) * 4;
-          const f32x16& ga = acc[fm][0];
-          const f32x16& ua = acc[fm][1];
+          const int j = j0 + (wn * (C::FN / 2) + pr) * 32 + g * 8 + (lane >> 5) * 4;
+          if (j >= n) continue;
           float gv[4], uv[4];
 #pragma unroll
           for (int q = 0; q < 4; ++q) {
-            gv[q] = ga[4 * g + q];
-            uv[q] = ua[4 * g + q];
+            gv[q] = acc[fm][2 * pr][4 * g + q];
+            uv[q] = acc[fm][2 * pr + 1][4 * g + q];
           }
           store_bf16x4(gr + j, gv[0], gv[1], gv[2], gv[3]);
           store_bf16x4(gr + n + j, uv[0], uv[1], uv[2], uv[3]);
-          store_bf16x4(hr + j, silu_f(gv[0]) * uv[0], silu_f(gv[1]) * uv[1],
-                       silu_f(gv[2]) * uv[2], silu_f(gv[3]) * uv[3]);
+          store_bf16x4(hr + j, silu_f(gv[0]) * uv[0], silu_f(gv[1]) * uv[1], silu_f(gv[2]) * uv[2],
+                       silu_f(gv[3]) * uv[3]);
         }
       }
     }
   }
 }
 
-// O = H W_dn^T + s (H A_dn) B_dn.   Tile: 128 rows x 128 of d.
-__global__ __launch_bounds__(NT) void k_down(const Layer L) {
-  using C = CfgMain;
-  __shared__ __attribute__((aligned(16))) bf16_t lds[C::LDS_ELEMS];
-  __shared__ int pre[MAX_ET + 1];
-  __shared__ int sh[4];
-  MSched sch;
-  sch.init<C::BM>(L, pre, sh);
-  const int n = L.n, d = L.d;
+// O = H W_dn^T + s (H A_dn) B_dn.   Tile: BM rows x BN of d.
+template <class C>
+__global__ __launch_bounds__(C::NT) __attribute__((amdgpu_waves_per_eu(C::OCC))) void k_down(const Layer L) {
+  MOE_GEMM_PROLOGUE(C)
+  const int n = L.n, d = L.d, r = L.r, rs = L.rs;
   const int ntn = cdiv(d, C::BN);
-  const int total = sch.total_m() * ntn;
+  const int total = pre[L.Et] * ntn;
   for (int t = first_tile(); t < total; t += gridDim.x) {
-    int e, mt, nt;
-    sch.decode(t, ntn, e, mt, nt);
-    const int row0 = seg_start(L, e) + mt * C::BM;
-    const int mrows = min(C::BM, seg_count(L, e) - mt * C::BM);
-    const int c0 = nt * C::BN;
+    const MTile T = decode_m<C::BM>(L, pre, t, ntn);
+    const int c0 = T.nt * C::BN;
+    const bool act = wave_active<C>(T.mrows, d - c0);
     f32x16 acc[C::FM][C::FN];
     zero_acc<C>(acc);
     {
-      auto A = kop<C::BM>(
-          [&](int m, float&) -> const bf16_t* {
-            return m < mrows ? L.h + (int64_t)(row0 + m) * n : nullptr;
-          },
-          n);
-      const bf16_t* wb = L.w_dn + (int64_t)e * d * n;
-      auto B = kop<C::BN>(
-          [&](int c, float&) -> const bf16_t* {
-            return c0 + c < d ? wb + (int64_t)(c0 + c) * n : nullptr;
-          },
-          n);
-      run_loop<C>(lds, A, B, n / BK, acc);
+      KOp<C::BM, C::NT, false, false> A(make_rsrc(L.h + (int64_t)T.row0 * n, (int64_t)T.mrows * n * 2),
+                                        [&](int m, float&) -> int64_t { return (int64_t)m * n * 2; }, n);
+      KOp<C::BN, C::NT, false, false> B(make_rsrc(L.w_dn + (int64_t)T.e * d * n, (int64_t)d * n * 2),
+                                        [&](int c, float&) -> int64_t {
+                                          return c0 + c < d ? (int64_t)(c0 + c) * n * 2 : -1;
+                                        },
+                                        n);
+      run_loop<C>(lds, A, B, n / BK, acc, act);
     }
     {
-      auto A = kop<C::BM>(
-          [&](int m, float&) -> const bf16_t* {
-            return m < mrows ? L.ha + (int64_t)(row0 + m) * L.rs : nullptr;
-          },
-          L.rs);
-      const bf16_t* bb = L.b_dn + (int64_t)e * L.r * d;
-      const float s = L.s;
-      auto B = mnop<C::BN>([&](int c) { return c0 + c < d ? c0 + c : -1; },
-                           [=](int kr, float& sc) -> const bf16_t* {
-                             sc = s;
-                             return bb + (int64_t)kr * d;
-                           },
-                           0, L.r, s != 1.0f);
-      run_loop<C>(lds, A, B, cdiv(L.rs, BK), acc);
+      KOp<C::BM, C::NT, true, false> A(make_rsrc(L.ha + (int64_t)T.row0 * rs, (int64_t)T.mrows * rs * 2),
+                                       [&](int m, float&) -> int64_t { return (int64_t)m * rs * 2; }, rs);
+      MNOp<C::BN, C::NT> B(make_rsrc(L.b_dn + (int64_t)T.e * r * d, (int64_t)r * d * 2),
+                           [&](int c) { return c0 + c < d ? c0 + c : -1; }, d * 2, L.s);
+      run_loop<C>(lds, A, B, cdiv(rs, BK), acc, act);
     }
-    for_each_quad<C>(acc, [&](int m, int c, int, float v0, float v1, float v2, float v3) {
-      if (m < mrows && c0 + c < d) store_bf16x4(L.o + (int64_t)(row0 + m) * d + c0 + c, v0, v1, v2, v3);
+    for_each_quad<C>(acc, [&](int m, int c, float v0, float v1, float v2, float v3) {
+      if (m < T.mrows && c0 + c < d)
+        store_bf16x4(L.o + (int64_t)(T.row0 + m) * d + c0 + c, v0, v1, v2, v3);
     });
   }
 }
 
 // ---------------------------------------------------------------- rank-r pre-passes
 
-// out[p, 0:rs] = act(p) . F   where the [K x rs] factor F is read either
-// column-wise from a [K, ra] array (A_gu, A_dn) or row-wise from a [r, K]
-// array (B_dn, B_gu: out = act . F^T).  Columns >= r come out as zeros.
+// out[p, 0:rs] = act(p) . F for the expert owning row p, where F is read
+// column-wise from a [K, ra] factor (A_gu, A_dn) or row-wise from a [r, K]
+// factor (B_dn, B_gu: out = act . F^T).  Columns in [r, rs) come out zero.
 enum PrepassKind { PRE_XA = 0, PRE_HA = 1, PRE_QDN = 2, PRE_QGU = 3 };
 
-template <int BN>
-__global__ __launch_bounds__(NT) void k_rank_prepass(const Layer L, int kind) {
-  using C = Cfg<128, BN, 4, 1>;
-  __shared__ __attribute__((aligned(16))) bf16_t lds[C::LDS_ELEMS];
-  __shared__ int pre[MAX_ET + 1];
-  __shared__ int sh[4];
-  MSched sch;
-  sch.init<C::BM>(L, pre, sh);
-  const int total = sch.total_m();
+// The contraction (d, n or 2n) can be split over `nsplit` workgroups per row
+// tile: each writes an fp32 partial [split][Ptot][rs] that k_prepass_reduce
+// sums in split order; with nsplit == 1 the tile writes bf16 directly.
+template <int BN, int KIND>
+__global__ __launch_bounds__(CfgSkinny<BN>::NT) __attribute__((amdgpu_waves_per_eu(2))) void k_rank_prepass(
+    const Layer L, int nsplit) {
+  using C = CfgSkinny<BN>;
+  MOE_GEMM_PROLOGUE(C)
   const int n = L.n, d = L.d, r = L.r, rs = L.rs, ra = L.ra;
+  const int K = KIND == PRE_XA || KIND == PRE_QDN ? d : KIND == PRE_HA ? n : 2 * n;
+  const int kchunk = cdiv(K / BK, nsplit) * BK;
+  const int total = pre[L.Et] * nsplit;
+  const rsrc_t rx = make_rsrc(KIND == PRE_XA ? L.x : L.dy, (int64_t)L.T * d * 2);
+  bf16_t* out = KIND == PRE_XA ? L.xa : KIND == PRE_HA ? L.ha : KIND == PRE_QDN ? L.qdn : L.qgu;
   for (int t = first_tile(); t < total; t += gridDim.x) {
-    int e, mt, nt;
-    sch.decode(t, 1, e, mt, nt);
-    const int row0 = seg_start(L, e) + mt * C::BM;
-    const int mrows = min(C::BM, seg_count(L, e) - mt * C::BM);
+    const int ks = t % nsplit;
+    const MTile T = decode_m<C::BM>(L, pre, t / nsplit, 1);
+    const int mrows = T.mrows;
+    const int kb = ks * kchunk;
+    const int kn = min(K - kb, kchunk);
+    const bool act = wave_active<C>(mrows, rs) && kn > 0;
     f32x16 acc[C::FM][C::FN];
     zero_acc<C>(acc);
-    bf16_t* out;
-    if (kind == PRE_XA) {
-      out = L.xa;
-      auto A = kop<C::BM>(
-          [&](int m, float&) -> const bf16_t* {
-            return m < mrows ? L.x + (int64_t)token_of(L, row0 + m) * d : nullptr;
+    if (KIND == PRE_XA) {
+      const int32_t* tok = L.tok + T.row0;
+      KOp<C::BM, C::NT, false, false> A(
+          rx,
+          [&](int m, float&) -> int64_t { return m < mrows ? ((int64_t)tok[m] * d + kb) * 2 : -1; },
+          kn);
+      MNOp<C::BN, C::NT> B(make_rsrc(L.a_gu + ((int64_t)T.e * d + kb) * ra, (int64_t)kn * ra * 2),
+                           [&](int c) { return c < rs ? c : -1; }, ra * 2);
+      run_loop<C>(lds, A, B, kn / BK, acc, act);
+    } else if (KIND == PRE_HA) {
+      KOp<C::BM, C::NT, false, false> A(
+          make_rsrc(L.h + (int64_t)T.row0 * n, (int64_t)mrows * n * 2),
+          [&](int m, float&) -> int64_t { return ((int64_t)m * n + kb) * 2; }, kn);
+      MNOp<C::BN, C::NT> B(make_rsrc(L.a_dn + ((int64_t)T.e * n + kb) * ra, (int64_t)kn * ra * 2),
+                           [&](int c) { return c < rs ? c : -1; }, ra * 2);
+      run_loop<C>(lds, A, B, kn / BK, acc, act);
+    } else if (KIND == PRE_QDN) {
+      const int32_t* tok = L.tok + T.row0;
+      const float* wgt = L.wgt + T.row0;
+      KOp<C::BM, C::NT, false, true> A(
+          rx,
+          [&](int m, float& sc) -> int64_t {
+            if (m >= mrows) return -1;
+            sc = wgt[m];
+            return ((int64_t)tok[m] * d + kb) * 2;
           },
-          d);
-      const bf16_t* fb = L.a_gu + (int64_t)e * d * ra;
-      auto B = mnop<C::BN>([&](int c) { return c < rs ? c : -1; },
-                           [=](int kr, float&) -> const bf16_t* { return fb + (int64_t)kr * ra; },
-                           0, d);
-      run_loop<C>(lds, A, B, d / BK, acc);
-    } else if (kind == PRE_HA) {
-      out = L.ha;
-      auto A = kop<C::BM>(
-          [&](int m, float&) -> const bf16_t* {
-            return m < mrows ? L.h + (int64_t)(row0 + m) * n : nullptr;
-          },
-          n);
-      const bf16_t* fb = L.a_dn + (int64_t)e * n * ra;
-      auto B = mnop<C::BN>([&](int c) { return c < rs ? c : -1; },
-                           [=](int kr, float&) -> const bf16_t* { return fb + (int64_t)kr * ra; },
-                           0, n);
-      run_loop<C>(lds, A, B, n / BK, acc);
-    } else if (kind == PRE_QDN) {
-      out = L.qdn;
-      auto A = kop<C::BM>(
-          [&](int m, float& sc) -> const bf16_t* {
-            if (m >= mrows) return nullptr;
-            sc = weight_of(L, row0 + m);
-            return L.dy + (int64_t)token_of(L, row0 + m) * d;
-          },
-          d, true);
-      const bf16_t* fb = L.b_dn + (int64_t)e * r * d;
-      auto B = kop<C::BN>(
-          [&](int c, float&) -> const bf16_t* { return c < r ? fb + (int64_t)c * d : nullptr; }, d);
-      run_loop<C>(lds, A, B, d / BK, acc);
+          kn);
+      KOp<C::BN, C::NT, false, false> B(
+          make_rsrc(L.b_dn + (int64_t)T.e * r * d, (int64_t)r * d * 2),
+          [&](int c, float&) -> int64_t { return c < r ? ((int64_t)c * d + kb) * 2 : -1; }, kn);
+      run_loop<C>(lds, A, B, kn / BK, acc, act);
     } else {
-      out = L.qgu;
-      auto A = kop<C::BM>(
-          [&](int m, float&) -> const bf16_t* {
-            return m < mrows ? L.dg + (int64_t)(row0 + m) * 2 * n : nullptr;
-          },
-          2 * n);
-      const bf16_t* fb = L.b_gu + (int64_t)e * r * 2 * n;
-      auto B = kop<C::BN>(
-          [&](int c, float&) -> const bf16_t* {
-            return c < r ? fb + (int64_t)c * 2 * n : nullptr;
-          },
-          2 * n);
-      run_loop<C>(lds, A, B, 2 * n / BK, acc);
+      KOp<C::BM, C::NT, false, false> A(
+          make_rsrc(L.dg + (int64_t)T.row0 * 2 * n, (int64_t)mrows * 2 * n * 2),
+          [&](int m, float&) -> int64_t { return ((int64_t)m * 2 * n + kb) * 2; }, kn);
+      KOp<C::BN, C::NT, false, false> B(
+          make_rsrc(L.b_gu + (int64_t)T.e * r * 2 * n, (int64_t)r * 2 * n * 2),
+          [&](int c, float&) -> int64_t { return c < r ? ((int64_t)c * 2 * n + kb) * 2 : -1; }, kn);
+      run_loop<C>(lds, A, B, kn / BK, acc, act);
     }
-    for_each_quad<C>(acc, [&](int m, int c, int, float v0, float v1, float v2, float v3) {
-      if (m < mrows && c < rs) store_bf16x4(out + (int64_t)(row0 + m) * rs + c, v0, v1, v2, v3);
-    });
+    if (nsplit == 1) {
+      for_each_quad<C>(acc, [&](int m, int c, float v0, float v1, float v2, float v3) {
+        if (m < mrows && c < rs) store_bf16x4(out + (int64_t)(T.row0 + m) * rs + c, v0, v1, v2, v3);
+      });
+    } else {
+      float* part = L.pre_partial + (int64_t)ks * L.Ptot * rs;
+      for_each_quad<C>(acc, [&](int m, int c, float v0, float v1, float v2, float v3) {
+        if (m < mrows && c < rs)
+          *(float4*)(part + (int64_t)(T.row0 + m) * rs + c) = make_float4(v0, v1, v2, v3);
+      });
+    }
+  }
+}
+
+// out[p, c] = bf16(sum over splits of the fp32 partials), 4 columns a thread.
+__global__ __launch_bounds__(256) void k_prepass_reduce(const Layer L, int kind, int nsplit) {
+  bf16_t* out = kind == PRE_XA ? L.xa : kind == PRE_HA ? L.ha : kind == PRE_QDN ? L.qdn : L.qgu;
+  const int64_t total4 = (int64_t)L.Ptot * L.rs / 4;
+  const int64_t plane = (int64_t)L.Ptot * L.rs;
+  for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < total4; i += (int64_t)gridDim.x * 256) {
+    float4 a = *(const float4*)(L.pre_partial + 4 * i);
+    for (int s = 1; s < nsplit; ++s) {
+      const float4 b = *(const float4*)(L.pre_partial + s * plane + 4 * i);
+      a.x += b.x;
+      a.y += b.y;
+      a.z += b.z;
+      a.w += b.w;
+    }
+    store_bf16x4(out + 4 * i, a.x, a.y, a.z, a.w);
   }
 }
 
@@ -598,58 +752,49 @@ __global__ __launch_bounds__(NT) void k_rank_prepass(const Layer L, int kind) {
 
 // dH = dO W_dn + s (dO B_dn^T) A_dn^T with dO = w * dY[token], then the SwiGLU
 // backward: dgate = dH * up * silu'(gate), dup = dH * silu(gate).
-__global__ __launch_bounds__(NT) void k_dh(const Layer L) {
-  using C = CfgMain;
-  __shared__ __attribute__((aligned(16))) bf16_t lds[C::LDS_ELEMS];
-  __shared__ int pre[MAX_ET + 1];
-  __shared__ int sh[4];
-  MSched sch;
-  sch.init<C::BM>(L, pre, sh);
-  const int n = L.n, d = L.d;
+template <class C>
+__global__ __launch_bounds__(C::NT) __attribute__((amdgpu_waves_per_eu(C::OCC))) void k_dh(const Layer L) {
+  MOE_GEMM_PROLOGUE(C)
+  const int n = L.n, d = L.d, rs = L.rs, ra = L.ra;
   const int ntn = cdiv(n, C::BN);
-  const int total = sch.total_m() * ntn;
+  const int total = pre[L.Et] * ntn;
+  const rsrc_t rdy = make_rsrc(L.dy, (int64_t)L.T * d * 2);
   for (int t = first_tile(); t < total; t += gridDim.x) {
-    int e, mt, nt;
-    sch.decode(t, ntn, e, mt, nt);
-    const int row0 = seg_start(L, e) + mt * C::BM;
-    const int mrows = min(C::BM, seg_count(L, e) - mt * C::BM);
-    const int j0 = nt * C::BN;
+    const MTile T = decode_m<C::BM>(L, pre, t, ntn);
+    const int j0 = T.nt * C::BN;
+    const bool act = wave_active<C>(T.mrows, n - j0);
     f32x16 acc[C::FM][C::FN];
     zero_acc<C>(acc);
     {
-      auto A = kop<C::BM>(
-          [&](int m, float& sc) -> const bf16_t* {
-            if (m >= mrows) return nullptr;
-            sc = weight_of(L, row0 + m);
-            return L.dy + (int64_t)token_of(L, row0 + m) * d;
+      const int32_t* tok = L.tok + T.row0;
+      const float* wgt = L.wgt + T.row0;
+      const int mrows = T.mrows;
+      KOp<C::BM, C::NT, false, true> A(
+          rdy,
+          [&](int m, float& sc) -> int64_t {
+            if (m >= mrows) return -1;
+            sc = wgt[m];
+            return (int64_t)tok[m] * d * 2;
           },
-          d, true);
-      const bf16_t* wb = L.w_dn + (int64_t)e * d * n;
-      auto B = mnop<C::BN>([&](int c) { return j0 + c < n ? j0 + c : -1; },
-                           [=](int kr, float&) -> const bf16_t* { return wb + (int64_t)kr * n; },
-                           0, d);
-      run_loop<C>(lds, A, B, d / BK, acc);
+          d);
+      MNOp<C::BN, C::NT> B(make_rsrc(L.w_dn + (int64_t)T.e * d * n, (int64_t)d * n * 2),
+                           [&](int c) { return j0 + c < n ? j0 + c : -1; }, n * 2);
+      run_loop<C>(lds, A, B, d / BK, acc, act);
     }
     {
-      auto A = kop<C::BM>(
-          [&](int m, float&) -> const bf16_t* {
-            return m < mrows ? L.qdn + (int64_t)(row0 + m) * L.rs : nullptr;
-          },
-          L.rs);
-      const bf16_t* ab = L.a_dn + (int64_t)e * n * L.ra;
-      const float s = L.s;
-      auto B = kop<C::BN>(
-          [&](int c, float& sc) -> const bf16_t* {
-            sc = s;
-            return j0 + c < n ? ab + (int64_t)(j0 + c) * L.ra : nullptr;
-          },
-          L.rs, s != 1.0f);
-      run_loop<C>(lds, A, B, cdiv(L.rs, BK), acc);
+      KOp<C::BM, C::NT, true, false> A(make_rsrc(L.qdn + (int64_t)T.row0 * rs, (int64_t)T.mrows * rs * 2),
+                                       [&](int m, float&) -> int64_t { return (int64_t)m * rs * 2; }, rs);
+      KOp<C::BN, C::NT, true, false> B(make_rsrc(L.a_dn + (int64_t)T.e * n * ra, (int64_t)n * ra * 2),
+                                       [&](int c, float&) -> int64_t {
+                                         return j0 + c < n ? (int64_t)(j0 + c) * ra * 2 : -1;
+                                       },
+                                       rs, L.s);
+      run_loop<C>(lds, A, B, cdiv(rs, BK), acc, act);
     }
-    for_each_quad<C>(acc, [&](int m, int c, int, float v0, float v1, float v2, float v3) {
+    for_each_quad<C>(acc, [&](int m, int c, float v0, float v1, float v2, float v3) {
       const int j = j0 + c;
-      if (m >= mrows || j >= n) return;
-      const int64_t p = row0 + m;
+      if (m >= T.mrows || j >= n) return;
+      const int64_t p = T.row0 + m;
       const uint2 gq = *(const uint2*)(L.g + p * 2 * n + j);
       const uint2 uq = *(const uint2*)(L.g + p * 2 * n + n + j);
       const float dh[4] = {v0, v1, v2, v3};
@@ -668,55 +813,40 @@ __global__ __launch_bounds__(NT) void k_dh(const Layer L) {
   }
 }
 
-// dX_pair = dG W_gu + s (dG B_gu^T) A_gu^T.   Tile: 128 rows x 128 of d.
-__global__ __launch_bounds__(NT) void k_dx(const Layer L) {
-  using C = CfgMain;
-  __shared__ __attribute__((aligned(16))) bf16_t lds[C::LDS_ELEMS];
-  __shared__ int pre[MAX_ET + 1];
-  __shared__ int sh[4];
-  MSched sch;
-  sch.init<C::BM>(L, pre, sh);
-  const int n = L.n, d = L.d;
+// dX_pair = dG W_gu + s (dG B_gu^T) A_gu^T.   Tile: BM rows x BN of d.
+template <class C>
+__global__ __launch_bounds__(C::NT) __attribute__((amdgpu_waves_per_eu(C::OCC))) void k_dx(const Layer L) {
+  MOE_GEMM_PROLOGUE(C)
+  const int n = L.n, d = L.d, rs = L.rs, ra = L.ra;
   const int ntn = cdiv(d, C::BN);
-  const int total = sch.total_m() * ntn;
+  const int total = pre[L.Et] * ntn;
   for (int t = first_tile(); t < total; t += gridDim.x) {
-    int e, mt, nt;
-    sch.decode(t, ntn, e, mt, nt);
-    const int row0 = seg_start(L, e) + mt * C::BM;
-    const int mrows = min(C::BM, seg_count(L, e) - mt * C::BM);
-    const int c0 = nt * C::BN;
+    const MTile T = decode_m<C::BM>(L, pre, t, ntn);
+    const int c0 = T.nt * C::BN;
+    const bool act = wave_active<C>(T.mrows, d - c0);
     f32x16 acc[C::FM][C::FN];
     zero_acc<C>(acc);
     {
-      auto A = kop<C::BM>(
-          [&](int m, float&) -> const bf16_t* {
-            return m < mrows ? L.dg + (int64_t)(row0 + m) * 2 * n : nullptr;
-          },
-          2 * n);
-      const bf16_t* wb = L.w_gu + (int64_t)e * 2 * n * d;
-      auto B = mnop<C::BN>([&](int c) { return c0 + c < d ? c0 + c : -1; },
-                           [=](int kr, float&) -> const bf16_t* { return wb + (int64_t)kr * d; },
-                           0, 2 * n);
-      run_loop<C>(lds, A, B, 2 * n / BK, acc);
+      KOp<C::BM, C::NT, false, false> A(
+          make_rsrc(L.dg + (int64_t)T.row0 * 2 * n, (int64_t)T.mrows * 2 * n * 2),
+          [&](int m, float&) -> int64_t { return (int64_t)m * 2 * n * 2; }, 2 * n);
+      MNOp<C::BN, C::NT> B(make_rsrc(L.w_gu + (int64_t)T.e * 2 * n * d, (int64_t)2 * n * d * 2),
+                           [&](int c) { return c0 + c < d ? c0 + c : -1; }, d * 2);
+      run_loop<C>(lds, A, B, 2 * n / BK, acc, act);
     }
     {
-      auto A = kop<C::BM>(
-          [&](int m, float&) -> const bf16_t* {
-            return m < mrows ? L.qgu + (int64_t)(row0 + m) * L.rs : nullptr;
-          },
-          L.rs);
-      const bf16_t* ab = L.a_gu + (int64_t)e * d * L.ra;
-      const float s = L.s;
-      auto B = kop<C::BN>(
-          [&](int c, float& sc) -> const bf16_t* {
-            sc = s;
-            return c0 + c < d ? ab + (int64_t)(c0 + c) * L.ra : nullptr;
-          },
-          L.rs, s != 1.0f);
-      run_loop<C>(lds, A, B, cdiv(L.rs, BK), acc);
+      KOp<C::BM, C::NT, true, false> A(make_rsrc(L.qgu + (int64_t)T.row0 * rs, (int64_t)T.mrows * rs * 2),
+                                       [&](int m, float&) -> int64_t { return (int64_t)m * rs * 2; }, rs);
+      KOp<C::BN, C::NT, true, false> B(make_rsrc(L.a_gu + (int64_t)T.e * d * ra, (int64_t)d * ra * 2),
+                                       [&](int c, float&) -> int64_t {
+                                         return c0 + c < d ? (int64_t)(c0 + c) * ra * 2 : -1;
+                                       },
+                                       rs, L.s);
+      run_loop<C>(lds, A, B, cdiv(rs, BK), acc, act);
     }
-    for_each_quad<C>(acc, [&](int m, int c, int, float v0, float v1, float v2, float v3) {
-      if (m < mrows && c0 + c < d) store_bf16x4(L.o + (int64_t)(row0 + m) * d + c0 + c, v0, v1, v2, v3);
+    for_each_quad<C>(acc, [&](int m, int c, float v0, float v1, float v2, float v3) {
+      if (m < T.mrows && c0 + c < d)
+        store_bf16x4(L.o + (int64_t)(T.row0 + m) * d + c0 + c, v0, v1, v2, v3);
     });
   }
 }
@@ -726,82 +856,72 @@ __global__ __launch_bounds__(NT) void k_dx(const Layer L) {
 // out[e] (M x N, fp32) = s * sum over expert e's rows p of U(p, m) V(p, c).
 // Both operands are read with the row index p as contraction index.  A chunk
 // of at most SPLITK_ROWS rows makes one partial; an expert with a single
-// chunk writes its result directly, otherwise into partial[slot] for the
+// chunk writes its result directly, otherwise into its partial slot for the
 // fixed-order reduction.
 enum GradKind { GR_DB_DN = 0, GR_DA_DN = 1, GR_DB_GU = 2, GR_DA_GU = 3 };
 
-template <int BM, int BN, int WM, int WN>
-__global__ __launch_bounds__(NT) void k_lora_grad(const Layer L, int kind, int M, int N) {
-  using C = Cfg<BM, BN, WM, WN>;
+template <class C, int KIND>
+__global__ __launch_bounds__(C::NT) __attribute__((amdgpu_waves_per_eu(C::OCC))) void k_lora_grad(const Layer L) {
+  constexpr int BM = C::BM, BN = C::BN, NT = C::NT;
   __shared__ __attribute__((aligned(16))) bf16_t lds[C::LDS_ELEMS];
   __shared__ int pre[MAX_ET + 1];
-  __shared__ int sh[4];
-  KSched sch;
-  sch.init(L, pre, sh);
+  __shared__ int sh[C::NW];
+  expert_prefix<NT>(L, pre, sh, [&](int e) { return cdiv(seg_count(L, e), SPLITK_ROWS); });
+  const int n = L.n, d = L.d, rs = L.rs;
+  int M, N;
+  grad_shape(KIND, d, n, L.r, M, N);
   const int nmt = cdiv(M, BM), nnt = cdiv(N, BN);
   const int per_slot = nmt * nnt;
-  const int total = sch.slots() * per_slot;
-  const int n = L.n, d = L.d, rs = L.rs;
-  float* outbase = kind == GR_DB_DN ? L.db_dn : kind == GR_DA_DN ? L.da_dn
-                 : kind == GR_DB_GU ? L.db_gu : L.da_gu;
+  const int total = pre[L.Et] * per_slot;
+  float* outbase = KIND == GR_DB_DN ? L.db_dn : KIND == GR_DA_DN ? L.da_dn
+                 : KIND == GR_DB_GU ? L.db_gu : L.da_gu;
+  float* partial = L.partial + L.partial_off[KIND];
+  const rsrc_t rx = make_rsrc(KIND == GR_DB_DN ? L.dy : L.x, (int64_t)L.T * d * 2);
   for (int t = first_tile(); t < total; t += gridDim.x) {
     const int slot = t / per_slot;
     const int rem = t - slot * per_slot;
     const int nt = rem / nmt, mt = rem - nt * nmt;
-    const int e = sch.expert_of_slot(slot);
+    const int e = find_expert(pre, L.Et, slot, 1);
     const int chunk = slot - pre[e];
     const int nchunk = pre[e + 1] - pre[e];
     const int kb = seg_start(L, e) + chunk * SPLITK_ROWS;
-    const int ke = min(seg_start(L, e) + seg_count(L, e), kb + SPLITK_ROWS);
+    const int kn = min(seg_count(L, e) - chunk * SPLITK_ROWS, SPLITK_ROWS);
     const int m0 = mt * BM, c0 = nt * BN;
-    const int nk = cdiv(ke - kb, BK);
+    const int nk = cdiv(kn, BK);
+    const bool act = wave_active<C>(M - m0, N - c0);
     f32x16 acc[C::FM][C::FN];
     zero_acc<C>(acc);
-    const Rows rw = rows_of(L);
-    const bf16_t *ha = L.ha, *hh = L.h, *qdn = L.qdn, *xa = L.xa, *dg = L.dg, *qgu = L.qgu;
-    const bf16_t *dy = L.dy, *xx = L.x;
-    if (kind == GR_DB_DN) {  // s (H A_dn)^T dO : M = r, N = d
-      auto A = mnop<BM>([&](int m) { return m0 + m < rs ? m0 + m : -1; },
-                        [=](int p, float&) -> const bf16_t* { return ha + (int64_t)p * rs; },
-                        kb, ke);
-      auto B = mnop<BN>([&](int c) { return c0 + c < d ? c0 + c : -1; },
-                        [=](int p, float& sc) -> const bf16_t* {
-                          sc = rw.weight(p);
-                          return dy + (int64_t)rw.token(p) * d;
-                        },
-                        kb, ke, true);
-      run_loop<C>(lds, A, B, nk, acc);
-    } else if (kind == GR_DA_DN) {  // s H^T Q_dn : M = n, N = r
-      auto A = mnop<BM>([&](int m) { return m0 + m < n ? m0 + m : -1; },
-                        [=](int p, float&) -> const bf16_t* { return hh + (int64_t)p * n; },
-                        kb, ke);
-      auto B = mnop<BN>([&](int c) { return c0 + c < rs ? c0 + c : -1; },
-                        [=](int p, float&) -> const bf16_t* { return qdn + (int64_t)p * rs; },
-                        kb, ke);
-      run_loop<C>(lds, A, B, nk, acc);
-    } else if (kind == GR_DB_GU) {  // s (X A_gu)^T dG : M = r, N = 2n
-      auto A = mnop<BM>([&](int m) { return m0 + m < rs ? m0 + m : -1; },
-                        [=](int p, float&) -> const bf16_t* { return xa + (int64_t)p * rs; },
-                        kb, ke);
-      auto B = mnop<BN>([&](int c) { return c0 + c < 2 * n ? c0 + c : -1; },
-                        [=](int p, float&) -> const bf16_t* { return dg + (int64_t)p * 2 * n; },
-                        kb, ke);
-      run_loop<C>(lds, A, B, nk, acc);
-    } else {  // s X^T Q_gu : M = d, N = r
-      auto A = mnop<BM>([&](int m) { return m0 + m < d ? m0 + m : -1; },
-                        [=](int p, float&) -> const bf16_t* {
-                          return xx + (int64_t)rw.token(p) * d;
-                        },
-                        kb, ke);
-      auto B = mnop<BN>([&](int c) { return c0 + c < rs ? c0 + c : -1; },
-                        [=](int p, float&) -> const bf16_t* { return qgu + (int64_t)p * rs; },
-                        kb, ke);
-      run_loop<C>(lds, A, B, nk, acc);
+    const rsrc_t rtok = make_rsrc(L.tok + kb, (int64_t)kn * 4);
+    const rsrc_t rwgt = make_rsrc(L.wgt + kb, (int64_t)kn * 4);
+    if (KIND == GR_DB_DN) {  // (H A_dn)^T dO : M = r, N = d
+      MNOp<BM, NT> A(make_rsrc(L.ha + (int64_t)kb * rs, (int64_t)kn * rs * 2),
+                     [&](int m) { return m0 + m < rs ? m0 + m : -1; }, rs * 2);
+      MNGather<BN, NT, true> B(rx, rtok, rwgt, [&](int c) { return c0 + c < d ? c0 + c : -1; }, d * 2,
+                               kn);
+      run_loop<C>(lds, A, B, nk, acc, act);
+    } else if (KIND == GR_DA_DN) {  // H^T Q_dn : M = n, N = r
+      MNOp<BM, NT> A(make_rsrc(L.h + (int64_t)kb * n, (int64_t)kn * n * 2),
+                     [&](int m) { return m0 + m < n ? m0 + m : -1; }, n * 2);
+      MNOp<BN, NT> B(make_rsrc(L.qdn + (int64_t)kb * rs, (int64_t)kn * rs * 2),
+                     [&](int c) { return c0 + c < rs ? c0 + c : -1; }, rs * 2);
+      run_loop<C>(lds, A, B, nk, acc, act);
+    } else if (KIND == GR_DB_GU) {  // (X A_gu)^T dG : M = r, N = 2n
+      MNOp<BM, NT> A(make_rsrc(L.xa + (int64_t)kb * rs, (int64_t)kn * rs * 2),
+                     [&](int m) { return m0 + m < rs ? m0 + m : -1; }, rs * 2);
+      MNOp<BN, NT> B(make_rsrc(L.dg + (int64_t)kb * 2 * n, (int64_t)kn * 2 * n * 2),
+                     [&](int c) { return c0 + c < 2 * n ? c0 + c : -1; }, 2 * n * 2);
+      run_loop<C>(lds, A, B, nk, acc, act);
+    } else {  // X^T Q_gu : M = d, N = r
+      MNGather<BM, NT, false> A(rx, rtok, rwgt, [&](int m) { return m0 + m < d ? m0 + m : -1; }, d * 2,
+                                kn);
+      MNOp<BN, NT> B(make_rsrc(L.qgu + (int64_t)kb * rs, (int64_t)kn * rs * 2),
+                     [&](int c) { return c0 + c < rs ? c0 + c : -1; }, rs * 2);
+      run_loop<C>(lds, A, B, nk, acc, act);
     }
     const bool direct = nchunk == 1;
-    float* out = direct ? outbase + (int64_t)e * M * N : L.partial + (int64_t)slot * M * N;
+    float* out = direct ? outbase + (int64_t)e * M * N : partial + (int64_t)slot * M * N;
     const float s = direct ? L.s : 1.0f;
-    for_each_quad<C>(acc, [&](int m, int c, int, float v0, float v1, float v2, float v3) {
+    for_each_quad<C>(acc, [&](int m, int c, float v0, float v1, float v2, float v3) {
       const int gm = m0 + m, gc = c0 + c;
       if (gm >= M) return;
       float* o = out + (int64_t)gm * N + gc;
@@ -817,29 +937,44 @@ __global__ __launch_bounds__(NT) void k_lora_grad(const Layer L, int kind, int M
   }
 }
 
-// out[e] = s * sum_chunks partial (experts with >= 2 chunks, summed in chunk
-// order), zeros for experts without rows; single-chunk experts are already
-// final.
-__global__ __launch_bounds__(NT) void k_grad_reduce(const Layer L, int kind, int M, int N) {
-  __shared__ int pre[MAX_ET + 1];
-  __shared__ int sh[4];
-  KSched sch;
-  sch.init(L, pre, sh);
+// For all four gradients at once (blockIdx.z = kind, blockIdx.y = expert):
+// out[e] = s * sum of the expert's partials in chunk order when it has >= 2
+// chunks, zeros when it has no rows; single-chunk experts were written by
+// the GEMM, so their blocks leave after one load.
+constexpr int RED_NT = 256;
+__global__ __launch_bounds__(RED_NT) void k_grad_reduce(const Layer L) {
+  const int e = blockIdx.y;
+  const int nchunk = cdiv(seg_count(L, e), SPLITK_ROWS);
+  if (nchunk == 1) return;
+  __shared__ int sh[RED_NT / 64];
+  // first partial slot of expert e: chunks of all earlier experts
+  int mine = 0;
+  for (int q = threadIdx.x; q < e; q += RED_NT) mine += cdiv(seg_count(L, q), SPLITK_ROWS);
+  int slot0;
+  block_excl_scan<RED_NT / 64>(mine, sh, &slot0);
+  const int kind = blockIdx.z;
+  int M, N;
+  grad_shape(kind, L.d, L.n, L.r, M, N);
   float* outbase = kind == GR_DB_DN ? L.db_dn : kind == GR_DA_DN ? L.da_dn
                  : kind == GR_DB_GU ? L.db_gu : L.da_gu;
+  const float* partial = L.partial + L.partial_off[kind];
   const int64_t MN = (int64_t)M * N;
-  const int e = blockIdx.y;
-  const int nchunk = pre[e + 1] - pre[e];
-  if (nchunk == 1) return;
   float* out = outbase + (int64_t)e * MN;
-  for (int64_t i = (int64_t)blockIdx.x * NT + threadIdx.x; i < MN; i += (int64_t)gridDim.x * NT) {
+  for (int64_t i = (int64_t)blockIdx.x * RED_NT + threadIdx.x; i < MN;
+       i += (int64_t)gridDim.x * RED_NT) {
     float acc = 0.0f;
-    for (int c = 0; c < nchunk; ++c) acc += L.partial[(int64_t)(pre[e] + c) * MN + i];
+    for (int c = 0; c < nchunk; ++c) acc += partial[(int64_t)(slot0 + c) * MN + i];
     out[i] = L.s * acc;
   }
 }
 
 // ---------------------------------------------------------------- launchers
+
+// Workgroups that fit on one CU at once, from the tile's LDS footprint.
+template <class C>
+constexpr int wg_per_cu() {
+  return (C::LDS_ELEMS * 2 + 4096) * 2 <= 160 * 1024 ? 2 : 1;
+}
 
 static int grid_for(int max_tiles, int per_cu, int ncu) {
   int g = std::min(max_tiles, per_cu * ncu);
@@ -849,82 +984,89 @@ static int grid_for(int max_tiles, int per_cu, int ncu) {
 
 static int mtiles_bound(const Layer& L, int BM) { return L.Ptot / BM + L.Et; }
 
+template <int KIND>
+static void launch_prepass(const Layer& L, hipStream_t st, const char* name) {
+  const int mt = mtiles_bound(L, 128);
+  const int K = KIND == PRE_XA || KIND == PRE_QDN ? L.d : KIND == PRE_HA ? L.n : 2 * L.n;
+  const int nsplit = prepass_splits(L.Ptot, L.Et, K, L.ncu);
+  if (L.rs <= 64) {
+    using C = CfgSkinny<64>;
+    MOE_LAUNCH(name, (k_rank_prepass<64, KIND>), dim3(grid_for(mt * nsplit, wg_per_cu<C>(), L.ncu)),
+               dim3(C::NT), 0, st, L, nsplit);
+  } else {
+    using C = CfgSkinny<128>;
+    MOE_LAUNCH(name, (k_rank_prepass<128, KIND>), dim3(grid_for(mt * nsplit, wg_per_cu<C>(), L.ncu)),
+               dim3(C::NT), 0, st, L, nsplit);
+  }
+  if (nsplit > 1) {
+    const int g = (int)std::min<int64_t>(cdiv64((int64_t)L.Ptot * L.rs / 4, 256), 4096);
+    MOE_LAUNCH("prepass_reduce", k_prepass_reduce, dim3(g), dim3(256), 0, st, L, KIND, nsplit);
+  }
+}
+
 hipError_t gemm_gate_up(const Layer& L, hipStream_t st) {
-  const int mt64 = mtiles_bound(L, 128);
-  if (L.rs <= 64)
-    MOE_LAUNCH("prepass_xa", k_rank_prepass<64>, dim3(grid_for(mt64, 2, L.ncu)), dim3(NT), 0, st, L,
-                       (int)PRE_XA);
-  else
-    MOE_LAUNCH("prepass_xa", k_rank_prepass<128>, dim3(grid_for(mt64, 2, L.ncu)), dim3(NT), 0, st, L,
-                       (int)PRE_XA);
-  MOE_LAUNCH("gate_up", k_gate_up, dim3(grid_for(mt64 * (L.n / 64), 2, L.ncu)), dim3(NT), 0, st, L);
+  using C = MainCfg<MOE_CFG_GU>::type;
+  launch_prepass<PRE_XA>(L, st, "prepass_xa");
+  const int tiles = mtiles_bound(L, C::BM) * cdiv(L.n, C::BN / 2);
+  MOE_LAUNCH("gate_up", k_gate_up<C>, dim3(grid_for(tiles, wg_per_cu<C>(), L.ncu)), dim3(C::NT), 0,
+             st, L);
   return hipGetLastError();
 }
 
 hipError_t gemm_down(const Layer& L, hipStream_t st) {
-  const int mt = mtiles_bound(L, 128);
-  if (L.rs <= 64)
-    MOE_LAUNCH("prepass_ha", k_rank_prepass<64>, dim3(grid_for(mt, 2, L.ncu)), dim3(NT), 0, st, L,
-                       (int)PRE_HA);
-  else
-    MOE_LAUNCH("prepass_ha", k_rank_prepass<128>, dim3(grid_for(mt, 2, L.ncu)), dim3(NT), 0, st, L,
-                       (int)PRE_HA);
-  MOE_LAUNCH("down", k_down, dim3(grid_for(mt * cdiv(L.d, 128), 2, L.ncu)), dim3(NT), 0, st, L);
+  using C = MainCfg<MOE_CFG_DN>::type;
+  launch_prepass<PRE_HA>(L, st, "prepass_ha");
+  const int tiles = mtiles_bound(L, C::BM) * cdiv(L.d, C::BN);
+  MOE_LAUNCH("down", k_down<C>, dim3(grid_for(tiles, wg_per_cu<C>(), L.ncu)), dim3(C::NT), 0, st, L);
   return hipGetLastError();
 }
 
 hipError_t gemm_dh(const Layer& L, hipStream_t st) {
-  const int mt = mtiles_bound(L, 128);
-  if (L.rs <= 64)
-    MOE_LAUNCH("prepass_qdn", k_rank_prepass<64>, dim3(grid_for(mt, 2, L.ncu)), dim3(NT), 0, st, L,
-                       (int)PRE_QDN);
-  else
-    MOE_LAUNCH("prepass_qdn", k_rank_prepass<128>, dim3(grid_for(mt, 2, L.ncu)), dim3(NT), 0, st, L,
-                       (int)PRE_QDN);
-  MOE_LAUNCH("dh", k_dh, dim3(grid_for(mt * cdiv(L.n, 128), 2, L.ncu)), dim3(NT), 0, st, L);
+  using C = MainCfg<MOE_CFG_DH>::type;
+  launch_prepass<PRE_QDN>(L, st, "prepass_qdn");
+  const int tiles = mtiles_bound(L, C::BM) * cdiv(L.n, C::BN);
+  MOE_LAUNCH("dh", k_dh<C>, dim3(grid_for(tiles, wg_per_cu<C>(), L.ncu)), dim3(C::NT), 0, st, L);
   return hipGetLastError();
 }
 
 hipError_t gemm_dx(const Layer& L, hipStream_t st) {
-  const int mt = mtiles_bound(L, 128);
-  if (L.rs <= 64)
-    MOE_LAUNCH("prepass_qgu", k_rank_prepass<64>, dim3(grid_for(mt, 2, L.ncu)), dim3(NT), 0, st, L,
-                       (int)PRE_QGU);
-  else
-    MOE_LAUNCH("prepass_qgu", k_rank_prepass<128>, dim3(grid_for(mt, 2, L.ncu)), dim3(NT), 0, st, L,
-                       (int)PRE_QGU);
-  MOE_LAUNCH("dx", k_dx, dim3(grid_for(mt * cdiv(L.d, 128), 2, L.ncu)), dim3(NT), 0, st, L);
+  using C = MainCfg<MOE_CFG_DX>::type;
+  launch_prepass<PRE_QGU>(L, st, "prepass_qgu");
+  const int tiles = mtiles_bound(L, C::BM) * cdiv(L.d, C::BN);
+  MOE_LAUNCH("dx", k_dx<C>, dim3(grid_for(tiles, wg_per_cu<C>(), L.ncu)), dim3(C::NT), 0, st, L);
   return hipGetLastError();
 }
 
-static const char* const kGradNames[4] = {"grad_db_dn", "grad_da_dn", "grad_db_gu", "grad_da_gu"};
-static const char* const kReduceNames[4] = {"reduce_db_dn", "reduce_da_dn", "reduce_db_gu",
-                                            "reduce_da_gu"};
-
-template <int BM, int BN, int WM, int WN>
-static void launch_grad(const Layer& L, int kind, int M, int N, hipStream_t st) {
+template <class C, int KIND>
+static void launch_grad(const Layer& L, hipStream_t st, const char* name) {
+  int M, N;
+  grad_shape(KIND, L.d, L.n, L.r, M, N);
   const int slots = L.Ptot / SPLITK_ROWS + L.Et;
-  const int tiles = slots * cdiv(M, BM) * cdiv(N, BN);
-  MOE_LAUNCH(kGradNames[kind], (k_lora_grad<BM, BN, WM, WN>), dim3(grid_for(tiles, 2, L.ncu)), dim3(NT), 0,
-                     st, L, kind, M, N);
-  const int64_t MN = (int64_t)M * N;
-  const int gx = (int)std::min<int64_t>(cdiv64(MN, NT), 64);
-  MOE_LAUNCH(kReduceNames[kind], k_grad_reduce, dim3(gx, L.Et), dim3(NT), 0, st, L, kind, M, N);
+  const int tiles = slots * cdiv(M, C::BM) * cdiv(N, C::BN);
+  MOE_LAUNCH(name, (k_lora_grad<C, KIND>), dim3(grid_for(tiles, wg_per_cu<C>(), L.ncu)), dim3(C::NT),
+             0, st, L);
 }
 
 hipError_t gemm_lora_grads(const Layer& L, hipStream_t st) {
-  const int r = L.r, n = L.n, d = L.d;
   if (L.rs <= 64) {
-    launch_grad<64, 128, 2, 2>(L, GR_DB_DN, r, d, st);
-    launch_grad<128, 64, 4, 1>(L, GR_DA_DN, n, r, st);
-    launch_grad<64, 128, 2, 2>(L, GR_DB_GU, r, 2 * n, st);
-    launch_grad<128, 64, 4, 1>(L, GR_DA_GU, d, r, st);
+    launch_grad<Cfg<64, 128, 2, 2>, GR_DB_DN>(L, st, "grad_db_dn");
+    launch_grad<Cfg<128, 64, 4, 1>, GR_DA_DN>(L, st, "grad_da_dn");
+    launch_grad<Cfg<64, 128, 2, 2>, GR_DB_GU>(L, st, "grad_db_gu");
+    launch_grad<Cfg<128, 64, 4, 1>, GR_DA_GU>(L, st, "grad_da_gu");
   } else {
-    launch_grad<128, 128, 2, 2>(L, GR_DB_DN, r, d, st);
-    launch_grad<128, 128, 2, 2>(L, GR_DA_DN, n, r, st);
-    launch_grad<128, 128, 2, 2>(L, GR_DB_GU, r, 2 * n, st);
-    launch_grad<128, 128, 2, 2>(L, GR_DA_GU, d, r, st);
+    launch_grad<Cfg<128, 128, 2, 2>, GR_DB_DN>(L, st, "grad_db_dn");
+    launch_grad<Cfg<128, 128, 2, 2>, GR_DA_DN>(L, st, "grad_da_dn");
+    launch_grad<Cfg<128, 128, 2, 2>, GR_DB_GU>(L, st, "grad_db_gu");
+    launch_grad<Cfg<128, 128, 2, 2>, GR_DA_GU>(L, st, "grad_da_gu");
   }
+  int64_t mn_max = 0;
+  for (int kind = 0; kind < 4; ++kind) {
+    int M, N;
+    grad_shape(kind, L.d, L.n, L.r, M, N);
+    mn_max = std::max<int64_t>(mn_max, (int64_t)M * N);
+  }
+  const int gx = (int)std::min<int64_t>(cdiv64(mn_max, RED_NT), 32);
+  MOE_LAUNCH("reduce_grads", k_grad_reduce, dim3(gx, L.Et, 4), dim3(RED_NT), 0, st, L);
   return hipGetLastError();
 }
 

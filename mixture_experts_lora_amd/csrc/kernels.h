@@ -50,15 +50,27 @@ struct Layer {
   float* db_gu;      // [Et, r, 2n]
   float* da_dn;      // [Et, n, r]
   float* db_dn;      // [Et, r, d]
-  float* partial;    // split-K partial sums
+  float* partial;    // split-K partial sums of the LoRA gradients
+  float* pre_partial;  // split-K partial sums of the rank-r pre-passes [split][Ptot][rs]
+  int64_t partial_off[4];  // float offset of each gradient's partial slots
+  const int32_t* tok;      // [Ptot] token of each sorted row (gather table)
+  const float* wgt;        // [Ptot] routing weight of each sorted row (1 for shared)
 };
+
+// Shape (M x N) of the four LoRA gradients: 0 dB_dn [r,d], 1 dA_dn [n,r],
+// 2 dB_gu [r,2n], 3 dA_gu [d,r].
+__host__ __device__ inline void grad_shape(int kind, int d, int n, int r, int& M, int& N) {
+  M = kind == 0 ? r : kind == 1 ? n : kind == 2 ? r : d;
+  N = kind == 0 ? d : kind == 1 ? r : kind == 2 ? 2 * n : r;
+}
 
 // Workspace carving shared by the size query and the launchers.
 struct WsLayout {
-  size_t o, dg, qdn, qgu, partial, a_gu_pack, a_dn_pack, total;
+  size_t o, dg, qdn, qgu, partial, pre_partial, a_gu_pack, a_dn_pack, total;
+  int64_t partial_off[4];
 };
 struct SavedLayout {
-  size_t g, h, xa, ha, total;
+  size_t g, h, xa, ha, tok, wgt, total;
 };
 WsLayout ws_layout(int64_t T, int d, int n, int E, int k, int r, int S);
 SavedLayout saved_layout(int64_t T, int d, int n, int E, int k, int r, int S);
@@ -78,6 +90,7 @@ hipError_t gemm_lora_grads(const Layer& L, hipStream_t st);  // dA, dB of both m
 // Element-wise / gather kernels (layer.hip).
 hipError_t launch_pack_a(const Layer& L, const bf16_t* a_gu_src, const bf16_t* a_dn_src,
                          bf16_t* a_gu_dst, bf16_t* a_dn_dst, hipStream_t st);
+hipError_t launch_gather_table(const Layer& L, int32_t* tok, float* wgt, hipStream_t st);
 hipError_t launch_combine(const Layer& L, bool weighted, const bf16_t* src, bf16_t* dst,
                           hipStream_t st);
 
@@ -94,5 +107,19 @@ void timing_post(hipStream_t st);
   } while (0)
 
 constexpr int SPLITK_ROWS = 2048;  // segment rows per split-K chunk of the LoRA grads
+constexpr int PREPASS_MAX_SPLIT = 4;
+
+// Contraction splits of a rank-r pre-pass: enough row tiles x splits to give
+// every CU about two workgroups, at most PREPASS_MAX_SPLIT, each split at
+// least 4 K steps of 64.
+inline int prepass_splits(int Ptot, int Et, int K, int ncu) {
+  const int mt = Ptot / 128 + Et;
+  // split only when the row tiles alone would leave most CUs idle
+  if (mt * 2 >= ncu) return 1;
+  int s = (2 * ncu + mt - 1) / mt;
+  s = s < 1 ? 1 : s > PREPASS_MAX_SPLIT ? PREPASS_MAX_SPLIT : s;
+  while (s > 1 && (K / 64) / s < 4) --s;
+  return s;
+}
 
 }  // namespace moe

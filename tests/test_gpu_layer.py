@@ -26,6 +26,8 @@ CASES = {
     "k_equals_E": LayerDims(64, 64, 64, 4, 4, 8),
     "one_token": LayerDims(1, 64, 64, 4, 2, 4),
     "wide_d320_zipf": LayerDims(700, 320, 192, 8, 3, 24, logits_recipe="zipf"),
+    # contraction long enough for the rank-r pre-passes to split over workgroups
+    "prepass_splits": LayerDims(200, 1024, 256, 4, 2, 16),
 }
 
 
