@@ -32,6 +32,7 @@
 //  - the schedule is derived on the device from the routing offsets: no
 //    host synchronisation, empty experts produce no tiles.
 #include <algorithm>
+#include <type_traits>
 
 #include "common.h"
 #include "kernels.h"
@@ -48,19 +49,27 @@ constexpr int MAX_ET = 512;
 
 // Tile configuration: BM x BN outputs per workgroup, WM x WN waves (64
 // threads each), PGR register stages of global prefetch (1 or 2).
-template <int BM_, int BN_, int WM_, int WN_, int PGR_ = MOE_PGR>
+template <int BM_, int BN_, int WM_, int WN_, int PGR_ = MOE_PGR, int DMA_NS_ = 0, int DBK_ = 64,
+          int OCC_ = 0>
 struct Cfg {
   static constexpr int BM = BM_, BN = BN_, WAVES_M = WM_, WAVES_N = WN_, PGR = PGR_;
+  // DMA_NS > 0: row-contiguous main-loop operands go global -> LDS directly
+  // through a ring of DMA_NS stages of DBK k each (unpadded, XOR-swizzled rows)
+  static constexpr int DMA_NS = DMA_NS_, DBK = DBK_;
+  static constexpr int DMA_STAGE = (BM_ + BN_) * DBK_;   // bf16 elements per ring stage
   static constexpr int NW = WM_ * WN_, NT = 64 * NW;
-  // waves per SIMD the register allocation must allow: two workgroups of 4
-  // waves, or one of 8
-  static constexpr int OCC = 2;
+  // waves per SIMD the register allocation must allow (default: two
+  // workgroups of 4 waves, or one of 8, unless the wave tile is large)
+  static constexpr int OCC = OCC_ ? OCC_ : (NW == 4 && (BM / WM_) * (BN / WN_) > 64 * 64) ? 1 : 2;
   static constexpr int TM = BM / WM_, TN = BN / WN_;
   static constexpr int FM = TM / 32, FN = TN / 32;
   static_assert(FM >= 1 && FN >= 1, "wave tile at least 32x32");
+  static_assert(DBK_ == 32 || DBK_ == 64, "DMA k step");
   static constexpr int A_ELEMS = BM * LDK, B_ELEMS = BN * LDK;
   static constexpr int STAGE = A_ELEMS + B_ELEMS;
-  static constexpr int LDS_ELEMS = 2 * STAGE;
+  // PGR 0: one LDS buffer, no prefetch (the short rank-r step of a DMA kernel)
+  static constexpr int REG_LDS = (PGR_ == 0 ? 1 : 2) * STAGE;
+  static constexpr int LDS_ELEMS = REG_LDS > DMA_NS_ * DMA_STAGE ? REG_LDS : DMA_NS_ * DMA_STAGE;
 };
 
 // ---------------------------------------------------------------- buffer loads
@@ -102,21 +111,19 @@ __device__ __forceinline__ uint32_t word_of(const uint4& v, int i) {
 // R rows of a K-contiguous source; row r starts at byte rowoff(r) of the
 // buffer (negative = a zero row).  Each thread moves 16-byte chunks; the K
 // offset of a step goes in the scalar offset.  KCHECK masks chunks at or past
-// kmax (narrow rank-r rows); SCALED multiplies each row by its own factor
-// (dO = w * dY); `cs` is a uniform factor (the LoRA scale), applied when != 1.
-template <int R, int NT, bool KCHECK, bool SCALED>
+// kmax (narrow rank-r rows); SCALED multiplies each row by its own factor.
+template <int R, int NT, bool KCHECK, bool SCALED, int NS = 3>
 struct KOp {
   static constexpr int CH = R * (BK / 8);
   static constexpr int PER = (CH + NT - 1) / NT;
   rsrc_t rs;
   uint32_t voff[PER];
   float scl[PER];
-  uint4 v[2][PER];
+  uint4 v[NS][PER];
   int kmax;
-  float cs;
 
   template <class RowFn>
-  __device__ KOp(rsrc_t r, RowFn rowoff, int kmax_, float cs_ = 1.0f) : rs(r), kmax(kmax_), cs(cs_) {
+  __device__ KOp(rsrc_t r, RowFn rowoff, int kmax_) : rs(r), kmax(kmax_) {
 #pragma unroll
     for (int i = 0; i < PER; ++i) {
       const int c = threadIdx.x + i * NT;
@@ -146,8 +153,7 @@ struct KOp {
       const int c = threadIdx.x + i * NT;
       if (CH % NT == 0 || c < CH) {
         uint4 w = v[S][i];
-        if (SCALED) w = scale8(w, scl[i] * cs);
-        else if (cs != 1.0f) w = scale8(w, cs);
+        if (SCALED) w = scale8(w, scl[i]);
         *(uint4*)(lds + (c >> 3) * LDK + (c & 7) * 8) = w;
       }
     }
@@ -172,19 +178,20 @@ __device__ __forceinline__ void store_block_t(bf16_t* lds, int kq, int mg, const
 // R columns of a source whose contraction index is its row index: element
 // (k, c) at byte k*ldb + 2*col(c) of the buffer (the buffer starts at the
 // first row of the contraction range and ends with its last row, so rows past
-// the range read as zero).  8 consecutive columns are contiguous.
-template <int R, int NT>
+// the range read as zero).  8 consecutive columns are contiguous.  WROWS
+// multiplies contraction row k by the fp32 weight at byte 4k of `rw`.
+template <int R, int NT, int NS = 3, bool WROWS = false>
 struct MNOp {
   static constexpr int NB = (BK / 4) * (R / 8);
   static constexpr int PER = (NB + NT - 1) / NT;
-  rsrc_t rs;
+  rsrc_t rs, rw;
   uint32_t colb[PER];
   uint32_t ldb;
-  float cs;
-  uint4 v[2][PER][4];
+  uint4 v[NS][PER][4];
+  uint4 wv[NS][PER];
 
   template <class ColFn>
-  __device__ MNOp(rsrc_t r, ColFn colfn, uint32_t ldb_, float cs_ = 1.0f) : rs(r), ldb(ldb_), cs(cs_) {
+  __device__ MNOp(rsrc_t r, ColFn colfn, uint32_t ldb_, rsrc_t rw_ = rsrc_t()) : rs(r), rw(rw_), ldb(ldb_) {
 #pragma unroll
     for (int i = 0; i < PER; ++i) {
       const int bi = threadIdx.x + i * NT;
@@ -200,6 +207,7 @@ struct MNOp {
 #pragma unroll
       for (int q = 0; q < 4; ++q)  // the row goes in the range-checked vector offset
         v[S][i][q] = bload16(rs, colb[i] + (uint32_t)(k0 + kq * 4 + q) * ldb, 0);
+      if (WROWS) wv[S][i] = bload16(rw, (uint32_t)(k0 + kq * 4) * 4u, 0);
     }
   }
   template <int S>
@@ -210,7 +218,8 @@ struct MNOp {
       if (NB % NT != 0 && bi >= NB) continue;
       uint4 w[4];
 #pragma unroll
-      for (int q = 0; q < 4; ++q) w[q] = cs != 1.0f ? scale8(v[S][i][q], cs) : v[S][i][q];
+      for (int q = 0; q < 4; ++q)
+        w[q] = WROWS ? scale8(v[S][i][q], __uint_as_float(word_of(wv[S][i], q))) : v[S][i][q];
       store_block_t(lds, bi & 15, bi >> 4, w);
     }
   }
@@ -219,7 +228,7 @@ struct MNOp {
 // As MNOp, but contraction row k is token tok[k] of a [T, ld] source (the
 // hidden states or the upstream gradient), optionally scaled by wgt[k].  The
 // gather indices of the next step are loaded one step ahead.
-template <int R, int NT, bool SCALED>
+template <int R, int NT, bool SCALED, int NS = 3>
 struct MNGather {
   static constexpr int NB = (BK / 4) * (R / 8);
   static constexpr int PER = (NB + NT - 1) / NT;
@@ -227,8 +236,8 @@ struct MNGather {
   uint32_t colb[PER];
   uint32_t ldb;
   int kmax;
-  uint4 v[2][PER][4];
-  float scl[2][PER][4];
+  uint4 v[NS][PER][4];
+  float scl[NS][PER][4];
   uint4 tn[PER], wn[PER];
 
   template <class ColFn>
@@ -300,6 +309,24 @@ __device__ __forceinline__ void mma_stage(const bf16_t* As, const bf16_t* Bs,
   }
 }
 
+// One K step of the three-stage pipeline: register stage S (step kt) is free
+// to take step kt+3, stage (S+1)%3 holds step kt+1 and goes to the other LDS
+// buffer after the MFMAs.
+template <class C, int S, class OA, class OB>
+__device__ __forceinline__ void run_step3(bf16_t* lds, OA& oa, OB& ob, int kt, int nk, int klast,
+                                          f32x16 (&acc)[C::FM][C::FN], bool active) {
+  bf16_t* cur = lds + (kt & 1) * C::STAGE;
+  bf16_t* nxt = lds + ((kt + 1) & 1) * C::STAGE;
+  oa.template fetch<S>(min((kt + 3) * BK, klast));
+  ob.template fetch<S>(min((kt + 3) * BK, klast));
+  mma_stage<C>(cur, cur + C::A_ELEMS, acc, active);
+  if (kt + 1 < nk) {
+    oa.template store<(S + 1) % 3>(nxt);
+    ob.template store<(S + 1) % 3>(nxt + C::A_ELEMS);
+  }
+  __syncthreads();
+}
+
 // Pipelined K loop over nk steps of 64.  Global loads run MOE_PGR steps ahead
 // of the MFMAs, LDS is double-buffered, one barrier per step.  Ends with a
 // barrier, so the LDS can be reused right after.
@@ -307,7 +334,17 @@ template <class C, class OA, class OB>
 __device__ __forceinline__ void run_loop(bf16_t* lds, OA& oa, OB& ob, int nk,
                                          f32x16 (&acc)[C::FM][C::FN], bool active = true) {
   if (nk <= 0) return;
-  if constexpr (C::PGR == 1) {
+  if constexpr (C::PGR == 0) {
+  for (int kt = 0; kt < nk; ++kt) {
+    oa.template fetch<0>(kt * BK);
+    ob.template fetch<0>(kt * BK);
+    oa.template store<0>(lds);
+    ob.template store<0>(lds + C::A_ELEMS);
+    __syncthreads();
+    mma_stage<C>(lds, lds + C::A_ELEMS, acc, active);
+    __syncthreads();
+  }
+  } else if constexpr (C::PGR == 1) {
   oa.template fetch<0>(0);
   ob.template fetch<0>(0);
   oa.template store<0>(lds);
@@ -326,6 +363,31 @@ __device__ __forceinline__ void run_loop(bf16_t* lds, OA& oa, OB& ob, int nk,
       ob.template store<0>(nxt + C::A_ELEMS);
     }
     __syncthreads();
+  }
+  } else if constexpr (C::PGR == 3) {
+  // three register stages: stage s holds step kt+s while step kt computes
+  const int klast = (nk - 1) * BK;
+  oa.template fetch<0>(0);
+  ob.template fetch<0>(0);
+  oa.template fetch<1>(min(BK, klast));
+  ob.template fetch<1>(min(BK, klast));
+  oa.template fetch<2>(min(2 * BK, klast));
+  ob.template fetch<2>(min(2 * BK, klast));
+  oa.template store<0>(lds);
+  ob.template store<0>(lds + C::A_ELEMS);
+  __syncthreads();
+  for (int kt = 0; kt < nk; kt += 6) {
+    run_step3<C, 0>(lds, oa, ob, kt, nk, klast, acc, active);
+    if (kt + 1 >= nk) break;
+    run_step3<C, 1>(lds, oa, ob, kt + 1, nk, klast, acc, active);
+    if (kt + 2 >= nk) break;
+    run_step3<C, 2>(lds, oa, ob, kt + 2, nk, klast, acc, active);
+    if (kt + 3 >= nk) break;
+    run_step3<C, 0>(lds, oa, ob, kt + 3, nk, klast, acc, active);
+    if (kt + 4 >= nk) break;
+    run_step3<C, 1>(lds, oa, ob, kt + 4, nk, klast, acc, active);
+    if (kt + 5 >= nk) break;
+    run_step3<C, 2>(lds, oa, ob, kt + 5, nk, klast, acc, active);
   }
   } else {
   // Look-ahead fetches are issued unconditionally (past the last step they
@@ -365,6 +427,175 @@ __device__ __forceinline__ void run_loop(bf16_t* lds, OA& oa, OB& ob, int nk,
     }
   }
   }
+}
+
+
+// ---------------------------------------------------------------- LDS-DMA operands
+
+// Buffer descriptor as four scalar registers (base, 16-bit stride 0,
+// num_records, the gfx9 raw-buffer word).
+typedef int int4v __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ int4v make_desc(const void* base, int64_t bytes) {
+  const uint64_t a = (uint64_t)(uintptr_t)base;
+  const int64_t cap = 0x7fffffff;
+  int4v d;
+  d.x = (int)(uint32_t)(a & 0xffffffffu);
+  d.y = (int)(uint32_t)((a >> 32) & 0xffffu);
+  d.z = (int)(bytes < cap ? bytes : cap);
+  d.w = 0x00020000;
+  return d;
+}
+
+// One buffer_load_dwordx4 ... lds: every lane's 16 bytes land in LDS at
+// lds_addr + 16 * lane (out-of-range lanes write zeros).  Issued from inline
+// asm so the compiler does not serialise LDS reads behind it; completion is
+// tracked with explicit vmcnt waits by the pipeline.
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"
+__device__ __forceinline__ void dma16(int4v desc, uint32_t voff, uint32_t soff, uint32_t lds_addr) {
+  asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, %3 offen lds"
+               :
+               : "s"(lds_addr), "v"(voff), "s"(desc), "s"(soff)
+               : "memory", "m0");
+}
+#pragma clang diagnostic pop
+
+// vmcnt wait with the other counters left alone (gfx9 s_waitcnt encoding).
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+
+// XOR swizzle of the 16-byte chunk position inside an LDS row of DBK bf16:
+// the 16 rows one ds_read_b128 quarter-wave touches (same chunk) land on 16
+// distinct 16-byte bank groups of the 256-byte bank window.
+template <int DBK>
+__device__ __forceinline__ int sw_chunk(int row, int c) {
+  constexpr int CPR = DBK / 8, RP = 256 / (DBK * 2);  // chunks per row, rows per window
+  return c ^ ((row / RP) & (CPR - 1));
+}
+
+// R rows x DBK k of a row-contiguous source, DMA'd into an unpadded swizzled
+// LDS panel [R][DBK].  One instruction fills 1 KiB (1024 / (2 DBK) rows);
+// the NW waves take the instructions in turn.  Row r starts at byte
+// rowoff(r) of the buffer (negative = zero row); KCHECK zeroes chunks at or
+// past kmax.
+template <int R, int NW, bool KCHECK, int DBK>
+struct KDma {
+  static constexpr int CPR = DBK / 8, RPI = 64 / CPR;
+  static constexpr int NI = R / (RPI * NW);
+  static_assert(NI * RPI * NW == R, "rows must split evenly over the waves");
+  int4v desc;
+  uint32_t voff[NI];
+  int kc[NI];
+  int kmax;
+
+  template <class RowFn>
+  __device__ KDma(int4v d, RowFn rowoff, int kmax_) : desc(d), kmax(kmax_) {
+    const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
+#pragma unroll
+    for (int j = 0; j < NI; ++j) {
+      const int row = RPI * (wid + j * NW) + lane / CPR;
+      const int c = sw_chunk<DBK>(row, lane % CPR);
+      const int64_t o = rowoff(row);
+      voff[j] = o < 0 ? OOB : (uint32_t)o + (uint32_t)(c * 16);
+      kc[j] = c * 8;
+    }
+  }
+  // LDS byte address of the panel's row 0 is `base`
+  __device__ __forceinline__ void issue(int k0, uint32_t base) {
+    const int wid = threadIdx.x >> 6;
+#pragma unroll
+    for (int j = 0; j < NI; ++j) {
+      uint32_t o = voff[j];
+      if (KCHECK && k0 + kc[j] >= kmax) o = OOB;
+      dma16(desc, o, (uint32_t)k0 * 2u, __builtin_amdgcn_readfirstlane(base + (wid + j * NW) * 1024));
+    }
+  }
+};
+
+// MFMAs of one ring stage over the wave's first NFM 32-row fragments (the
+// rest of its rows are padding).  Fragment rows are 32-aligned, so the
+// swizzle of a lane's row is the same in every fragment.
+template <class C, int NFM>
+__device__ __forceinline__ void mma_stage_sw(const bf16_t* As, const bf16_t* Bs,
+                                             f32x16 (&acc)[C::FM][C::FN]) {
+  if constexpr (NFM > 0) {
+    constexpr int DBK = C::DBK;
+    const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
+    const int wm = wid / C::WAVES_N, wn = wid % C::WAVES_N;
+    const int l = lane & 31;
+    const bf16_t* ab = As + (wm * C::TM + l) * DBK;
+    const bf16_t* bb = Bs + (wn * C::TN + l) * DBK;
+#pragma unroll
+    for (int kk = 0; kk < DBK / 16; ++kk) {
+      const int c = sw_chunk<DBK>(l, kk * 2 + (lane >> 5)) * 8;
+      uint4 a[NFM], b[C::FN];
+#pragma unroll
+      for (int fm = 0; fm < NFM; ++fm) a[fm] = *(const uint4*)(ab + fm * 32 * DBK + c);
+#pragma unroll
+      for (int fn = 0; fn < C::FN; ++fn) b[fn] = *(const uint4*)(bb + fn * 32 * DBK + c);
+#pragma unroll
+      for (int fm = 0; fm < NFM; ++fm)
+#pragma unroll
+        for (int fn = 0; fn < C::FN; ++fn) acc[fm][fn] = mfma32(b[fn], a[fm], acc[fm][fn]);
+    }
+  }
+}
+
+// K loop over nk steps of DBK with both operands DMA'd through a ring of
+// C::DMA_NS LDS stages, issued DMA_NS-1 steps ahead (past the last step the
+// issue re-reads the last step into a stage nobody reads).  One barrier per
+// step; ends with every DMA drained and a barrier, so the LDS can be reused.
+template <class C, int NFM, class DA, class DB>
+__device__ __forceinline__ void run_loop_dma(bf16_t* lds, DA& da, DB& db, int nk,
+                                             f32x16 (&acc)[C::FM][C::FN]) {
+  constexpr int NS = C::DMA_NS, PD = NS - 1, DBK = C::DBK;
+  constexpr int PER_STAGE = DA::NI + DB::NI;  // DMA instructions per wave per stage
+  if (nk <= 0) return;
+  const uint32_t base = (uint32_t)(uintptr_t)lds;
+  const int klast = (nk - 1) * DBK;
+  auto issue = [&](int step, int slot) {
+    const int k0 = min(step * DBK, klast);
+    const uint32_t sb = base + (uint32_t)slot * C::DMA_STAGE * 2;
+    da.issue(k0, sb);
+    db.issue(k0, sb + C::BM * DBK * 2);
+  };
+#pragma unroll
+  for (int s = 0; s < PD; ++s) issue(s, s);
+  int slot = 0;
+  for (int kt = 0; kt < nk; ++kt) {
+    wait_vmcnt<(PD - 1) * PER_STAGE>();
+    __syncthreads();
+    issue(kt + PD, slot == 0 ? NS - 1 : slot - 1);
+    const bf16_t* cur = lds + slot * C::DMA_STAGE;
+    mma_stage_sw<C, NFM>(cur, cur + C::BM * DBK, acc);
+    slot = slot + 1 == NS ? 0 : slot + 1;
+  }
+  wait_vmcnt<0>();
+  __syncthreads();
+}
+
+// Calls f(std::integral_constant<int, v>) with v the wave's number of 32-row
+// fragments holding valid rows (0 when its columns are all padding), rounded
+// up to a multiple of STEP (2 for eight fragments, to bound code size).
+template <int V, int STEP, class F>
+__device__ __forceinline__ void nfm_dispatch(int nfm, F& f) {
+  if constexpr (V <= 0) {
+    f(std::integral_constant<int, 0>());
+  } else {
+    if (nfm > V - STEP) f(std::integral_constant<int, V>());
+    else nfm_dispatch<V - STEP, STEP>(nfm, f);
+  }
+}
+template <class C, class F>
+__device__ __forceinline__ void with_nfm(int mrows, int ncols, F f) {
+  const int wid = threadIdx.x >> 6;
+  const int wm = wid / C::WAVES_N, wn = wid % C::WAVES_N;
+  int nfm = wn * C::TN < ncols ? cdiv(mrows - wm * C::TM, 32) : 0;
+  nfm = __builtin_amdgcn_readfirstlane(max(0, min(C::FM, nfm)));
+  nfm_dispatch<C::FM, (C::FM > 4 ? 2 : 1)>(nfm, f);
 }
 
 template <class C>
@@ -507,6 +738,28 @@ template <> struct MainCfg<4> { using type = Cfg<128, 256, 2, 2, 1>; };  // 4 wa
 template <> struct MainCfg<5> { using type = Cfg<128, 128, 2, 2, 1>; };  // 4 waves of 64x64
 template <> struct MainCfg<6> { using type = Cfg<256, 128, 4, 2, 2>; };  // 8 waves of 64x64
 template <> struct MainCfg<7> { using type = Cfg<128, 256, 2, 4, 2>; };  // 8 waves of 64x64
+template <> struct MainCfg<8> { using type = Cfg<128, 256, 2, 4, 3>; };  // 8 waves of 64x64
+template <> struct MainCfg<9> { using type = Cfg<128, 128, 2, 2, 3>; };  // 4 waves of 64x64
+template <> struct MainCfg<10> { using type = Cfg<256, 256, 2, 2, 1>; };  // 4 waves of 128x128
+template <> struct MainCfg<11> { using type = Cfg<256, 128, 2, 2, 1>; };  // 4 waves of 128x64
+// LDS-DMA main loops (forward GEMMs only): unpadded swizzled ring stages;
+// the rank-r step runs unpipelined through one padded LDS buffer
+template <> struct MainCfg<12> { using type = Cfg<256, 256, 2, 2, 0, 2, 64>; };     // 4 waves of 128x128
+template <> struct MainCfg<13> { using type = Cfg<256, 128, 2, 2, 0, 3, 64>; };     // 4 waves of 128x64
+template <> struct MainCfg<14> { using type = Cfg<128, 256, 1, 4, 0, 3, 64>; };     // 4 waves of 128x64
+template <> struct MainCfg<15> { using type = Cfg<256, 256, 4, 2, 0, 4, 32>; };     // 8 waves of 64x128
+template <> struct MainCfg<16> { using type = Cfg<256, 256, 4, 2, 0, 2, 64>; };     // 8 waves of 64x128
+template <> struct MainCfg<17> { using type = Cfg<128, 256, 2, 2, 0, 3, 32, 2>; };  // 4 waves of 64x128, 2 WG/CU
+template <> struct MainCfg<18> { using type = Cfg<256, 256, 2, 2, 0, 4, 32>; };     // 4 waves of 128x128
+template <> struct MainCfg<19> { using type = Cfg<128, 256, 1, 4, 0, 4, 32>; };     // 4 waves of 128x64
+template <> struct MainCfg<20> { using type = Cfg<128, 128, 2, 2, 0, 4, 32, 2>; };  // 4 waves of 64x64, 2 WG/CU
+template <> struct MainCfg<21> { using type = Cfg<128, 256, 1, 4, 0, 3, 32, 2>; };  // 4 waves of 128x64, 2 WG/CU
+template <> struct MainCfg<22> { using type = Cfg<256, 128, 4, 1, 0, 3, 32, 2>; };  // 4 waves of 64x128, 2 WG/CU
+template <> struct MainCfg<23> { using type = Cfg<128, 256, 1, 4, 0, 6, 32>; };     // 4 waves of 128x64, deep ring
+template <> struct MainCfg<24> { using type = Cfg<128, 256, 2, 2, 0, 6, 32>; };     // 4 waves of 64x128, deep ring
+template <> struct MainCfg<25> { using type = Cfg<256, 128, 4, 1, 0, 6, 32>; };     // 4 waves of 64x128, deep ring
+template <> struct MainCfg<26> { using type = Cfg<128, 256, 2, 4, 0, 6, 32>; };     // 8 waves of 64x64, deep ring
+template <> struct MainCfg<27> { using type = Cfg<256, 256, 4, 2, 0, 4, 32>; };     // 8 waves of 64x128
 #ifndef MOE_CFG_GU
 #define MOE_CFG_GU 7
 #endif
@@ -552,7 +805,22 @@ __global__ __launch_bounds__(C::NT) __attribute__((amdgpu_waves_per_eu(C::OCC)))
     const bool act = wave_active<C>(T.mrows, 2 * (n - j0));
     f32x16 acc[C::FM][C::FN];
     zero_acc<C>(acc);
-    {
+    if constexpr (C::DMA_NS > 0) {
+      const int32_t* tok = L.tok + T.row0;
+      const int mrows = T.mrows;
+      KDma<C::BM, C::NW, false, C::DBK> A(
+          make_desc(L.x, (int64_t)L.T * d * 2),
+          [&](int m) -> int64_t { return m < mrows ? (int64_t)tok[m] * d * 2 : -1; }, d);
+      KDma<C::BN, C::NW, false, C::DBK> B(
+          make_desc(L.w_gu + (int64_t)T.e * 2 * n * d, (int64_t)2 * n * d * 2),
+          [&](int c) -> int64_t {
+            return j0 + (c >> 6) * 32 + (c & 31) < n ? (int64_t)gu_row(n, j0, c) * d * 2 : -1;
+          },
+          d);
+      with_nfm<C>(T.mrows, 2 * (n - j0), [&](auto NF) {
+        run_loop_dma<C, decltype(NF)::value>(lds, A, B, d / C::DBK, acc);
+      });
+    } else {
       const int32_t* tok = L.tok + T.row0;
       const int mrows = T.mrows;
       KOp<C::BM, C::NT, false, false> A(
@@ -573,7 +841,7 @@ __global__ __launch_bounds__(C::NT) __attribute__((amdgpu_waves_per_eu(C::OCC)))
                            [&](int c) {
                              return j0 + (c >> 6) * 32 + (c & 31) < n ? gu_row(n, j0, c) : -1;
                            },
-                           2 * n * 2, L.s);
+                           2 * n * 2);
       run_loop<C>(lds, A, B, cdiv(rs, BK), acc, act);
     }
     // SwiGLU epilogue: a lane's fragments 2p (gate) and 2p+1 (up) cover the
@@ -622,7 +890,18 @@ __global__ __launch_bounds__(C::NT) __attribute__((amdgpu_waves_per_eu(C::OCC)))
     const bool act = wave_active<C>(T.mrows, d - c0);
     f32x16 acc[C::FM][C::FN];
     zero_acc<C>(acc);
-    {
+    if constexpr (C::DMA_NS > 0) {
+      const int mrows = T.mrows;
+      KDma<C::BM, C::NW, false, C::DBK> A(
+          make_desc(L.h + (int64_t)T.row0 * n, (int64_t)T.mrows * n * 2),
+          [&](int m) -> int64_t { return m < mrows ? (int64_t)m * n * 2 : -1; }, n);
+      KDma<C::BN, C::NW, false, C::DBK> B(
+          make_desc(L.w_dn + (int64_t)T.e * d * n, (int64_t)d * n * 2),
+          [&](int c) -> int64_t { return c0 + c < d ? (int64_t)(c0 + c) * n * 2 : -1; }, n);
+      with_nfm<C>(T.mrows, d - c0, [&](auto NF) {
+        run_loop_dma<C, decltype(NF)::value>(lds, A, B, n / C::DBK, acc);
+      });
+    } else {
       KOp<C::BM, C::NT, false, false> A(make_rsrc(L.h + (int64_t)T.row0 * n, (int64_t)T.mrows * n * 2),
                                         [&](int m, float&) -> int64_t { return (int64_t)m * n * 2; }, n);
       KOp<C::BN, C::NT, false, false> B(make_rsrc(L.w_dn + (int64_t)T.e * d * n, (int64_t)d * n * 2),
@@ -636,7 +915,7 @@ __global__ __launch_bounds__(C::NT) __attribute__((amdgpu_waves_per_eu(C::OCC)))
       KOp<C::BM, C::NT, true, false> A(make_rsrc(L.ha + (int64_t)T.row0 * rs, (int64_t)T.mrows * rs * 2),
                                        [&](int m, float&) -> int64_t { return (int64_t)m * rs * 2; }, rs);
       MNOp<C::BN, C::NT> B(make_rsrc(L.b_dn + (int64_t)T.e * r * d, (int64_t)r * d * 2),
-                           [&](int c) { return c0 + c < d ? c0 + c : -1; }, d * 2, L.s);
+                           [&](int c) { return c0 + c < d ? c0 + c : -1; }, d * 2);
       run_loop<C>(lds, A, B, cdiv(rs, BK), acc, act);
     }
     for_each_quad<C>(acc, [&](int m, int c, float v0, float v1, float v2, float v3) {
@@ -648,9 +927,11 @@ __global__ __launch_bounds__(C::NT) __attribute__((amdgpu_waves_per_eu(C::OCC)))
 
 // ---------------------------------------------------------------- rank-r pre-passes
 
-// out[p, 0:rs] = act(p) . F for the expert owning row p, where F is read
+// out[p, 0:rs] = s * act(p) . F for the expert owning row p, where F is read
 // column-wise from a [K, ra] factor (A_gu, A_dn) or row-wise from a [r, K]
-// factor (B_dn, B_gu: out = act . F^T).  Columns in [r, rs) come out zero.
+// factor (B_dn, B_gu: out = act . F^T), and act is X[token], H, dY[token]
+// (without the routing weight) or dG.  Columns in [r, rs) come out zero.
+// Every consumer of these rank-r rows takes the LoRA scale from them.
 enum PrepassKind { PRE_XA = 0, PRE_HA = 1, PRE_QDN = 2, PRE_QGU = 3 };
 
 // The contraction (d, n or 2n) can be split over `nsplit` workgroups per row
@@ -694,14 +975,9 @@ __global__ __launch_bounds__(CfgSkinny<BN>::NT) __attribute__((amdgpu_waves_per_
       run_loop<C>(lds, A, B, kn / BK, acc, act);
     } else if (KIND == PRE_QDN) {
       const int32_t* tok = L.tok + T.row0;
-      const float* wgt = L.wgt + T.row0;
-      KOp<C::BM, C::NT, false, true> A(
+      KOp<C::BM, C::NT, false, false> A(
           rx,
-          [&](int m, float& sc) -> int64_t {
-            if (m >= mrows) return -1;
-            sc = wgt[m];
-            return ((int64_t)tok[m] * d + kb) * 2;
-          },
+          [&](int m, float&) -> int64_t { return m < mrows ? ((int64_t)tok[m] * d + kb) * 2 : -1; },
           kn);
       KOp<C::BN, C::NT, false, false> B(
           make_rsrc(L.b_dn + (int64_t)T.e * r * d, (int64_t)r * d * 2),
@@ -716,15 +992,17 @@ __global__ __launch_bounds__(CfgSkinny<BN>::NT) __attribute__((amdgpu_waves_per_
           [&](int c, float&) -> int64_t { return c < r ? ((int64_t)c * 2 * n + kb) * 2 : -1; }, kn);
       run_loop<C>(lds, A, B, kn / BK, acc, act);
     }
+    const float sc = L.s;
     if (nsplit == 1) {
       for_each_quad<C>(acc, [&](int m, int c, float v0, float v1, float v2, float v3) {
-        if (m < mrows && c < rs) store_bf16x4(out + (int64_t)(T.row0 + m) * rs + c, v0, v1, v2, v3);
+        if (m < mrows && c < rs)
+          store_bf16x4(out + (int64_t)(T.row0 + m) * rs + c, sc * v0, sc * v1, sc * v2, sc * v3);
       });
     } else {
       float* part = L.pre_partial + (int64_t)ks * L.Ptot * rs;
       for_each_quad<C>(acc, [&](int m, int c, float v0, float v1, float v2, float v3) {
         if (m < mrows && c < rs)
-          *(float4*)(part + (int64_t)(T.row0 + m) * rs + c) = make_float4(v0, v1, v2, v3);
+          *(float4*)(part + (int64_t)(T.row0 + m) * rs + c) = make_float4(sc * v0, sc * v1, sc * v2, sc * v3);
       });
     }
   }
@@ -750,7 +1028,8 @@ __global__ __launch_bounds__(256) void k_prepass_reduce(const Layer L, int kind,
 
 // ---------------------------------------------------------------- backward, dX side
 
-// dH = dO W_dn + s (dO B_dn^T) A_dn^T with dO = w * dY[token], then the SwiGLU
+// dH = w * (dY[token] W_dn + Q_dn A_dn^T) with Q_dn = s dY[token] B_dn^T
+// (dO = w dY[token] is the gradient of the expert output), then the SwiGLU
 // backward: dgate = dH * up * silu'(gate), dup = dH * silu(gate).
 template <class C>
 __global__ __launch_bounds__(C::NT) __attribute__((amdgpu_waves_per_eu(C::OCC))) void k_dh(const Layer L) {
@@ -767,16 +1046,9 @@ __global__ __launch_bounds__(C::NT) __attribute__((amdgpu_waves_per_eu(C::OCC)))
     zero_acc<C>(acc);
     {
       const int32_t* tok = L.tok + T.row0;
-      const float* wgt = L.wgt + T.row0;
       const int mrows = T.mrows;
-      KOp<C::BM, C::NT, false, true> A(
-          rdy,
-          [&](int m, float& sc) -> int64_t {
-            if (m >= mrows) return -1;
-            sc = wgt[m];
-            return (int64_t)tok[m] * d * 2;
-          },
-          d);
+      KOp<C::BM, C::NT, false, false> A(
+          rdy, [&](int m, float&) -> int64_t { return m < mrows ? (int64_t)tok[m] * d * 2 : -1; }, d);
       MNOp<C::BN, C::NT> B(make_rsrc(L.w_dn + (int64_t)T.e * d * n, (int64_t)d * n * 2),
                            [&](int c) { return j0 + c < n ? j0 + c : -1; }, n * 2);
       run_loop<C>(lds, A, B, d / BK, acc, act);
@@ -788,7 +1060,7 @@ __global__ __launch_bounds__(C::NT) __attribute__((amdgpu_waves_per_eu(C::OCC)))
                                        [&](int c, float&) -> int64_t {
                                          return j0 + c < n ? (int64_t)(j0 + c) * ra * 2 : -1;
                                        },
-                                       rs, L.s);
+                                       rs);
       run_loop<C>(lds, A, B, cdiv(rs, BK), acc, act);
     }
     for_each_quad<C>(acc, [&](int m, int c, float v0, float v1, float v2, float v3) {
@@ -797,7 +1069,8 @@ __global__ __launch_bounds__(C::NT) __attribute__((amdgpu_waves_per_eu(C::OCC)))
       const int64_t p = T.row0 + m;
       const uint2 gq = *(const uint2*)(L.g + p * 2 * n + j);
       const uint2 uq = *(const uint2*)(L.g + p * 2 * n + n + j);
-      const float dh[4] = {v0, v1, v2, v3};
+      const float w = L.wgt[p];
+      const float dh[4] = {w * v0, w * v1, w * v2, w * v3};
       const float gv[4] = {bf2f(gq.x & 0xffff), bf2f(gq.x >> 16), bf2f(gq.y & 0xffff), bf2f(gq.y >> 16)};
       const float uv[4] = {bf2f(uq.x & 0xffff), bf2f(uq.x >> 16), bf2f(uq.y & 0xffff), bf2f(uq.y >> 16)};
       float dgt[4], dup[4];
@@ -841,7 +1114,7 @@ __global__ __launch_bounds__(C::NT) __attribute__((amdgpu_waves_per_eu(C::OCC)))
                                        [&](int c, float&) -> int64_t {
                                          return c0 + c < d ? (int64_t)(c0 + c) * ra * 2 : -1;
                                        },
-                                       rs, L.s);
+                                       rs);
       run_loop<C>(lds, A, B, cdiv(rs, BK), acc, act);
     }
     for_each_quad<C>(acc, [&](int m, int c, float v0, float v1, float v2, float v3) {
@@ -853,8 +1126,9 @@ __global__ __launch_bounds__(C::NT) __attribute__((amdgpu_waves_per_eu(C::OCC)))
 
 // ---------------------------------------------------------------- LoRA gradients
 
-// out[e] (M x N, fp32) = s * sum over expert e's rows p of U(p, m) V(p, c).
-// Both operands are read with the row index p as contraction index.  A chunk
+// out[e] (M x N, fp32) = sum over expert e's rows p of U(p, m) V(p, c); the
+// LoRA scale s is already inside the rank-r rows (s X A_gu, s H A_dn, Q_dn,
+// Q_gu).  Both operands are read with the row index p as contraction index.  A chunk
 // of at most SPLITK_ROWS rows makes one partial; an expert with a single
 // chunk writes its result directly, otherwise into its partial slot for the
 // fixed-order reduction.
@@ -893,19 +1167,19 @@ __global__ __launch_bounds__(C::NT) __attribute__((amdgpu_waves_per_eu(C::OCC)))
     zero_acc<C>(acc);
     const rsrc_t rtok = make_rsrc(L.tok + kb, (int64_t)kn * 4);
     const rsrc_t rwgt = make_rsrc(L.wgt + kb, (int64_t)kn * 4);
-    if (KIND == GR_DB_DN) {  // (H A_dn)^T dO : M = r, N = d
+    if (KIND == GR_DB_DN) {  // (s H A_dn)^T (w dY[token]) : M = r, N = d
       MNOp<BM, NT> A(make_rsrc(L.ha + (int64_t)kb * rs, (int64_t)kn * rs * 2),
                      [&](int m) { return m0 + m < rs ? m0 + m : -1; }, rs * 2);
       MNGather<BN, NT, true> B(rx, rtok, rwgt, [&](int c) { return c0 + c < d ? c0 + c : -1; }, d * 2,
                                kn);
       run_loop<C>(lds, A, B, nk, acc, act);
-    } else if (KIND == GR_DA_DN) {  // H^T Q_dn : M = n, N = r
+    } else if (KIND == GR_DA_DN) {  // H^T (w Q_dn) : M = n, N = r
       MNOp<BM, NT> A(make_rsrc(L.h + (int64_t)kb * n, (int64_t)kn * n * 2),
                      [&](int m) { return m0 + m < n ? m0 + m : -1; }, n * 2);
-      MNOp<BN, NT> B(make_rsrc(L.qdn + (int64_t)kb * rs, (int64_t)kn * rs * 2),
-                     [&](int c) { return c0 + c < rs ? c0 + c : -1; }, rs * 2);
+      MNOp<BN, NT, 3, true> B(make_rsrc(L.qdn + (int64_t)kb * rs, (int64_t)kn * rs * 2),
+                              [&](int c) { return c0 + c < rs ? c0 + c : -1; }, rs * 2, rwgt);
       run_loop<C>(lds, A, B, nk, acc, act);
-    } else if (KIND == GR_DB_GU) {  // (X A_gu)^T dG : M = r, N = 2n
+    } else if (KIND == GR_DB_GU) {  // (s X A_gu)^T dG : M = r, N = 2n
       MNOp<BM, NT> A(make_rsrc(L.xa + (int64_t)kb * rs, (int64_t)kn * rs * 2),
                      [&](int m) { return m0 + m < rs ? m0 + m : -1; }, rs * 2);
       MNOp<BN, NT> B(make_rsrc(L.dg + (int64_t)kb * 2 * n, (int64_t)kn * 2 * n * 2),
@@ -920,25 +1194,24 @@ __global__ __launch_bounds__(C::NT) __attribute__((amdgpu_waves_per_eu(C::OCC)))
     }
     const bool direct = nchunk == 1;
     float* out = direct ? outbase + (int64_t)e * M * N : partial + (int64_t)slot * M * N;
-    const float s = direct ? L.s : 1.0f;
     for_each_quad<C>(acc, [&](int m, int c, float v0, float v1, float v2, float v3) {
       const int gm = m0 + m, gc = c0 + c;
       if (gm >= M) return;
       float* o = out + (int64_t)gm * N + gc;
       if ((N & 3) == 0) {
-        if (gc < N) *(float4*)o = make_float4(s * v0, s * v1, s * v2, s * v3);
+        if (gc < N) *(float4*)o = make_float4(v0, v1, v2, v3);
       } else {
         const float vv[4] = {v0, v1, v2, v3};
 #pragma unroll
         for (int q = 0; q < 4; ++q)
-          if (gc + q < N) o[q] = s * vv[q];
+          if (gc + q < N) o[q] = vv[q];
       }
     });
   }
 }
 
 // For all four gradients at once (blockIdx.z = kind, blockIdx.y = expert):
-// out[e] = s * sum of the expert's partials in chunk order when it has >= 2
+// out[e] = sum of the expert's partials in chunk order when it has >= 2
 // chunks, zeros when it has no rows; single-chunk experts were written by
 // the GEMM, so their blocks leave after one load.
 constexpr int RED_NT = 256;
@@ -964,7 +1237,7 @@ __global__ __launch_bounds__(RED_NT) void k_grad_reduce(const Layer L) {
        i += (int64_t)gridDim.x * RED_NT) {
     float acc = 0.0f;
     for (int c = 0; c < nchunk; ++c) acc += partial[(int64_t)(slot0 + c) * MN + i];
-    out[i] = L.s * acc;
+    out[i] = acc;
   }
 }
 
