@@ -81,6 +81,10 @@ hipError_t launch_route(const float* logits, int64_t T, int E, int k, int32_t* i
                         int32_t* pair_pos, void* ws, hipStream_t st);
 
 // Grouped GEMM launchers (gemm.hip).
+// Streamed main GEMMs (stream.hip): the product only, without the pre-pass.
+hipError_t stream_gate_up(const Layer& L, hipStream_t st);
+hipError_t stream_down(const Layer& L, hipStream_t st);
+hipError_t stream_dx(const Layer& L, hipStream_t st);
 hipError_t gemm_gate_up(const Layer& L, hipStream_t st);   // G, H  (+ X A_gu pre-pass)
 hipError_t gemm_down(const Layer& L, hipStream_t st);      // O     (+ H A_dn pre-pass)
 hipError_t gemm_dh(const Layer& L, hipStream_t st);        // dG    (+ dO B_dn^T pre-pass)

@@ -1,0 +1,505 @@
+// Streamed grouped GEMMs: the four expert products of the layer
+//   gate_up  G = X[tok] W_gu^T + (s X A_gu) B_gu,   H = silu(gate) * up
+//   down     O = H W_dn^T + (s H A_dn) B_dn
+//   dh       dH = w (dY[tok] W_dn + Q_dn A_dn^T),   dG = SwiGLU'(dH; G)
+//   dx       dX_pair = dG W_gu + Q_gu A_gu^T
+// over the ragged per-expert row segments (Unsloth faster-MoE page, "What is
+// torch._grouped_mm?"), with the LoRA term kept split as a rank-r product
+// added into the same accumulator ("Faster LoRA MoE training").
+//
+// One persistent workgroup per CU runs ONE pipeline over its whole work
+// list: every step moves a 256 x 32 panel of each operand from global memory
+// straight into LDS (buffer_load_dwordx4 ... lds), through a ring of four
+// stages issued three steps ahead.  The step stream runs through a tile's
+// base K steps, then its rank-r steps, then on into the next tile, so the
+// pipeline never drains between tiles: the next tile's first panels are in
+// flight while the current tile's epilogue writes its outputs.
+//
+//  - tile 256 x 256, 4 waves of 128 x 128 (v_mfma_f32_32x32x16_bf16, fp32
+//    accumulation, operands swapped so a lane owns 4 consecutive columns);
+//  - row-contiguous panels are stored [256 rows][32 k] with the 16-byte chunk
+//    of row r at position c ^ ((r >> 2) & 3), read with ds_read_b128;
+//  - panels whose contraction index is the row index in memory (W_dn and
+//    W_gu in the backward, B_dn and B_gu in the forward) are stored
+//    [32 k][256 columns] with chunk c of row k at c ^ 4 (k & 3), and read
+//    with ds_read_b64_tr_b16, which hands each lane 4 consecutive k of one
+//    column: two of them make one MFMA operand;
+//  - rows past a segment, columns past a matrix and k past the rank get an
+//    out-of-range buffer offset and land in LDS as zeros;
+//  - the gather indices (token of each sorted row) of the next tile are
+//    DMA'd into LDS a whole tile ahead, so building the next tile's row
+//    offsets needs no global load in the loop;
+#include <algorithm>
+
+#include "common.h"
+#include "gemm_util.h"
+#include "kernels.h"
+
+namespace moe {
+namespace {
+
+constexpr int SBM = 256, SBN = 256;             // tile
+constexpr int SWM = 2, SWN = 2;                 // wave grid
+constexpr int SNW = SWM * SWN, SNT = 64 * SNW;  // 4 waves
+constexpr int STM = SBM / SWM, STN = SBN / SWN; // 128 x 128 per wave
+constexpr int SFM = STM / 32, SFN = STN / 32;   // 4 x 4 fragments
+constexpr int SK = 32;                          // k per ring stage
+constexpr int SNS = 4, SPD = SNS - 1;           // ring stages, issue distance
+constexpr int PANEL = SBM * SK;                 // bf16 elements of one operand panel
+constexpr int SSTAGE = 2 * PANEL;               // A panel then B panel
+constexpr int NI = PANEL * 2 / 1024 / SNW;      // DMA instructions per wave per panel
+constexpr int PER = 2 * NI;                     // per wave per stage
+static_assert(NI * SNW * 1024 == PANEL * 2, "panel split");
+
+enum StreamKind { SK_GU = 0, SK_DN = 1, SK_DH = 2, SK_DX = 3 };
+
+typedef short v4s __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) v4s lds_v4s;
+
+template <int KIND>
+struct SP {
+  static constexpr bool A_GATHER = KIND == SK_GU || KIND == SK_DH;
+  static constexpr bool B_MAIN_MN = KIND == SK_DH || KIND == SK_DX;
+  static constexpr bool B_LORA_MN = KIND == SK_GU || KIND == SK_DN;
+};
+
+template <int KIND>
+__device__ __forceinline__ int s_ntn(const Layer& L) {
+  return KIND == SK_GU ? cdiv(L.n, SBN / 2) : KIND == SK_DH ? cdiv(L.n, SBN) : cdiv(L.d, SBN);
+}
+template <int KIND>
+__device__ __forceinline__ int s_kmain(const Layer& L) {
+  return KIND == SK_GU || KIND == SK_DH ? L.d : KIND == SK_DN ? L.n : 2 * L.n;
+}
+
+struct STile {
+  int t, e, nt, row0, mrows;
+};
+
+__device__ __forceinline__ STile s_decode(const int* pre, const int* segst, int Et, int t, int ntn) {
+  STile T;
+  T.t = t;
+  T.e = __builtin_amdgcn_readfirstlane(find_expert(pre, Et, t, ntn));
+  const int local = t - pre[T.e] * ntn;
+  const int nm = pre[T.e + 1] - pre[T.e];
+  T.nt = __builtin_amdgcn_readfirstlane(local / nm);
+  const int mt = local - T.nt * nm;
+  T.row0 = __builtin_amdgcn_readfirstlane(segst[T.e] + mt * SBM);
+  T.mrows = __builtin_amdgcn_readfirstlane(min(SBM, segst[T.e + 1] - T.row0));
+  return T;
+}
+
+// Per-lane constants of the two panel layouts.
+//  K panel, instruction j of wave w: row 16 (w + 4 j) + lane / 4, physical
+//  chunk lane % 4 holding logical chunk lck = (lane & 3) ^ ((lane >> 4) & 3).
+//  MN panel, instruction j of wave w: k row 2 (w + 4 j) + lane / 32, physical
+//  chunk lane % 32 holding logical chunk lcm = (lane & 31) ^ fsw.
+__device__ __forceinline__ int s_lck() {
+  const int lane = threadIdx.x & 63;
+  return (lane & 3) ^ ((lane >> 4) & 3);
+}
+__device__ __forceinline__ int s_lcm() {
+  const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
+  return (lane & 31) ^ ((2 * (wid & 1) + (lane >> 5)) * 4);
+}
+__device__ __forceinline__ int s_krow(int j) {
+  const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
+  return 2 * (wid + j * SNW) + (lane >> 5);
+}
+__device__ __forceinline__ int s_prow(int j) {
+  const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
+  return 16 * (wid + j * SNW) + (lane >> 2);
+}
+
+// Issue cursor: the tile whose panels are being issued, its descriptors and
+// per-lane offsets, and the next step to issue.
+struct SIssue {
+  int4v da_m, db_m, da_l, db_l;
+  uint32_t va_m[NI], vb_m[NI], va_l[NI], vb_l[NI];
+  uint32_t ldb_bm, ldb_bl;  // byte stride of the MN-panel sources (k rows)
+  int step, smain, stot;
+};
+
+template <int KIND>
+__device__ __forceinline__ void s_setup(const Layer& L, const STile& T, const int* tok, SIssue& S) {
+  const int n = L.n, d = L.d, rs = L.rs, ra = L.ra, r = L.r;
+  const int lck = s_lck(), lcm = s_lcm();
+  const int e = T.e, row0 = T.row0, mrows = T.mrows;
+  S.smain = s_kmain<KIND>(L) / SK;
+  S.stot = S.smain + cdiv(rs, SK);
+  S.step = 0;
+  S.ldb_bm = 0;
+  S.ldb_bl = 0;
+  // A main
+  if constexpr (KIND == SK_GU || KIND == SK_DH) {
+    S.da_m = make_desc(KIND == SK_GU ? L.x : L.dy, (int64_t)L.T * d * 2);
+#pragma unroll
+    for (int j = 0; j < NI; ++j) {
+      const int m = s_prow(j);
+      S.va_m[j] = m < mrows ? (uint32_t)tok[m] * (uint32_t)(d * 2) + lck * 16 : OOB;
+    }
+  } else {
+    const int lda = KIND == SK_DN ? n : 2 * n;
+    const bf16_t* src = KIND == SK_DN ? L.h : L.dg;
+    S.da_m = make_desc(src + (int64_t)row0 * lda, (int64_t)mrows * lda * 2);
+#pragma unroll
+    for (int j = 0; j < NI; ++j) {
+      const int m = s_prow(j);
+      S.va_m[j] = m < mrows ? (uint32_t)m * (uint32_t)(lda * 2) + lck * 16 : OOB;
+    }
+  }
+  // A rank-r
+  {
+    const bf16_t* src = KIND == SK_GU ? L.xa : KIND == SK_DN ? L.ha : KIND == SK_DH ? L.qdn : L.qgu;
+    S.da_l = make_desc(src + (int64_t)row0 * rs, (int64_t)mrows * rs * 2);
+#pragma unroll
+    for (int j = 0; j < NI; ++j) {
+      const int m = s_prow(j);
+      S.va_l[j] = m < mrows ? (uint32_t)m * (uint32_t)(rs * 2) + lck * 16 : OOB;
+    }
+  }
+  // B main and B rank-r
+  if constexpr (KIND == SK_GU) {
+    const int j0 = T.nt * (SBN / 2);
+    S.db_m = make_desc(L.w_gu + (int64_t)e * 2 * n * d, (int64_t)2 * n * d * 2);
+#pragma unroll
+    for (int j = 0; j < NI; ++j) {
+      const int c = s_prow(j);
+      const bool ok = j0 + (c >> 6) * 32 + (c & 31) < n;
+      S.vb_m[j] = ok ? (uint32_t)gu_row(n, j0, c) * (uint32_t)(d * 2) + lck * 16 : OOB;
+    }
+    S.db_l = make_desc(L.b_gu + (int64_t)e * r * 2 * n, (int64_t)r * 2 * n * 2);
+    S.ldb_bl = 2 * n * 2;
+    const int c = lcm * 8;  // tile column of this lane's chunk (8 columns, one gate/up group)
+    const bool ok = j0 + (c >> 6) * 32 + (c & 31) < n;
+#pragma unroll
+    for (int j = 0; j < NI; ++j)
+      S.vb_l[j] = ok ? (uint32_t)s_krow(j) * S.ldb_bl + (uint32_t)gu_row(n, j0, c) * 2 : OOB;
+  } else if constexpr (KIND == SK_DN) {
+    const int c0 = T.nt * SBN;
+    S.db_m = make_desc(L.w_dn + (int64_t)e * d * n, (int64_t)d * n * 2);
+#pragma unroll
+    for (int j = 0; j < NI; ++j) {
+      const int c = s_prow(j);
+      S.vb_m[j] = c0 + c < d ? (uint32_t)(c0 + c) * (uint32_t)(n * 2) + lck * 16 : OOB;
+    }
+    S.db_l = make_desc(L.b_dn + (int64_t)e * r * d, (int64_t)r * d * 2);
+    S.ldb_bl = d * 2;
+    const int col = c0 + lcm * 8;
+#pragma unroll
+    for (int j = 0; j < NI; ++j) S.vb_l[j] = col < d ? (uint32_t)s_krow(j) * S.ldb_bl + (uint32_t)col * 2 : OOB;
+  } else if constexpr (KIND == SK_DH) {
+    const int j0 = T.nt * SBN;
+    S.db_m = make_desc(L.w_dn + (int64_t)e * d * n, (int64_t)d * n * 2);
+    S.ldb_bm = n * 2;
+    const int col = j0 + lcm * 8;
+#pragma unroll
+    for (int j = 0; j < NI; ++j) S.vb_m[j] = col < n ? (uint32_t)s_krow(j) * S.ldb_bm + (uint32_t)col * 2 : OOB;
+    S.db_l = make_desc(L.a_dn + (int64_t)e * n * ra, (int64_t)n * ra * 2);
+#pragma unroll
+    for (int j = 0; j < NI; ++j) {
+      const int c = s_prow(j);
+      S.vb_l[j] = j0 + c < n ? (uint32_t)(j0 + c) * (uint32_t)(ra * 2) + lck * 16 : OOB;
+    }
+  } else {
+    const int c0 = T.nt * SBN;
+    S.db_m = make_desc(L.w_gu + (int64_t)e * 2 * n * d, (int64_t)2 * n * d * 2);
+    S.ldb_bm = d * 2;
+    const int col = c0 + lcm * 8;
+#pragma unroll
+    for (int j = 0; j < NI; ++j) S.vb_m[j] = col < d ? (uint32_t)s_krow(j) * S.ldb_bm + (uint32_t)col * 2 : OOB;
+    S.db_l = make_desc(L.a_gu + (int64_t)e * d * ra, (int64_t)d * ra * 2);
+#pragma unroll
+    for (int j = 0; j < NI; ++j) {
+      const int c = s_prow(j);
+      S.vb_l[j] = c0 + c < d ? (uint32_t)(c0 + c) * (uint32_t)(ra * 2) + lck * 16 : OOB;
+    }
+  }
+}
+
+// Issue step `step` of the cursor's tile into the ring stage at LDS byte
+// address `sb` (A panel, then B panel).
+template <int KIND>
+__device__ __forceinline__ void s_issue(const SIssue& S, int step, uint32_t sb, int rs, int r) {
+  const int wid = threadIdx.x >> 6;
+  const uint32_t ma = sb, mb = sb + PANEL * 2;
+  if (step < S.smain) {
+    const int k0 = step * SK;
+#pragma unroll
+    for (int j = 0; j < NI; ++j)
+      dma16(S.da_m, S.va_m[j], (uint32_t)k0 * 2u, __builtin_amdgcn_readfirstlane(ma + (wid + j * SNW) * 1024));
+#pragma unroll
+    for (int j = 0; j < NI; ++j)
+      dma16(S.db_m, S.vb_m[j], SP<KIND>::B_MAIN_MN ? (uint32_t)k0 * S.ldb_bm : (uint32_t)k0 * 2u,
+            __builtin_amdgcn_readfirstlane(mb + (wid + j * SNW) * 1024));
+  } else {
+    const int k0 = (step - S.smain) * SK;
+    const int kc = s_lck() * 8;
+#pragma unroll
+    for (int j = 0; j < NI; ++j)
+      dma16(S.da_l, k0 + kc < rs ? S.va_l[j] : OOB, (uint32_t)k0 * 2u,
+            __builtin_amdgcn_readfirstlane(ma + (wid + j * SNW) * 1024));
+#pragma unroll
+    for (int j = 0; j < NI; ++j) {
+      if constexpr (SP<KIND>::B_LORA_MN)
+        dma16(S.db_l, k0 + s_krow(j) < r ? S.vb_l[j] : OOB, (uint32_t)k0 * S.ldb_bl,
+              __builtin_amdgcn_readfirstlane(mb + (wid + j * SNW) * 1024));
+      else
+        dma16(S.db_l, k0 + kc < rs ? S.vb_l[j] : OOB, (uint32_t)k0 * 2u,
+              __builtin_amdgcn_readfirstlane(mb + (wid + j * SNW) * 1024));
+    }
+  }
+}
+
+// MFMAs of one ring stage, k = 32: the wave's 4 x 4 fragments.  (Padding rows
+// are multiplied too: branching around fragments splits the accumulator's
+// live range and the register allocator then copies it through memory.)
+template <bool BMN>
+__device__ __forceinline__ void s_mma(const bf16_t* As, const bf16_t* Bs, f32x16 (&acc)[SFM][SFN]) {
+  const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
+  const int wm = wid / SWN, wn = wid % SWN;
+  const int l = lane & 31;
+  const char* ab = (const char*)As + (wm * STM + l) * (SK * 2);
+  const int swz = (l >> 2) & 3;
+  // MN panel: 16-lane group g reads k rows 8 (g >> 1) + q (+4 in the second
+  // read) at columns 16 (g & 1) + 4 rr of the fragment; the transposing read
+  // gives lane (g, j) the 4 k values of column 16 (g & 1) + j.
+  const int g = lane >> 4, q = (lane >> 2) & 3, rr = lane & 3;
+#pragma unroll
+  for (int kk = 0; kk < SK / 16; ++kk) {
+    const int c = ((kk * 2 + (lane >> 5)) ^ swz) * 16;
+    uint4 a[SFM], b[SFN];
+#pragma unroll
+    for (int fm = 0; fm < SFM; ++fm) a[fm] = *(const uint4*)(ab + fm * 32 * (SK * 2) + c);
+    if constexpr (!BMN) {
+      const char* bb = (const char*)Bs + (wn * STN + l) * (SK * 2);
+#pragma unroll
+      for (int fn = 0; fn < SFN; ++fn) b[fn] = *(const uint4*)(bb + fn * 32 * (SK * 2) + c);
+    } else {
+      const int krow = kk * 16 + 8 * (g >> 1) + q;
+      const int kx = (krow & 3) * 4;
+#pragma unroll
+      for (int fn = 0; fn < SFN; ++fn) {
+        const int col = wn * STN + fn * 32 + 16 * (g & 1) + 4 * rr;
+        const char* p = (const char*)Bs + krow * (SBN * 2) + (((col >> 3) ^ kx) * 16) + (col & 7) * 2;
+        const v4s lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s*)p);
+        const v4s hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s*)(p + 4 * SBN * 2));
+        b[fn] = make_uint4((uint32_t)(uint16_t)lo[0] | ((uint32_t)(uint16_t)lo[1] << 16),
+                           (uint32_t)(uint16_t)lo[2] | ((uint32_t)(uint16_t)lo[3] << 16),
+                           (uint32_t)(uint16_t)hi[0] | ((uint32_t)(uint16_t)hi[1] << 16),
+                           (uint32_t)(uint16_t)hi[2] | ((uint32_t)(uint16_t)hi[3] << 16));
+      }
+    }
+#pragma unroll
+    for (int fm = 0; fm < SFM; ++fm)
+#pragma unroll
+      for (int fn = 0; fn < SFN; ++fn) acc[fm][fn] = mfma32(b[fn], a[fm], acc[fm][fn]);
+  }
+}
+
+// Epilogue, through LDS.  The accumulators stay in AGPRs until they are
+// written (ds_write takes AGPR data): a wave stages a pair of neighbouring
+// 32 x 32 fp32 fragments in its private 8 KiB of the ring stage consumed
+// last (rows of 64 floats, 16-byte chunk c of row m at c ^ (m & 15)), then
+// reads back half a row per lane and writes full 128-byte row segments.
+// Fragment (fm, fn) of the wave covers rows wm 128 + fm 32 + 0..31 and tile
+// columns wn 128 + fn 32 + 0..31; lane l holds row l % 32, columns
+// 8 g + 4 (l / 32) + 0..3 in elements 4 g + 0..3.
+__device__ __forceinline__ void s_stage_pair(float* wl, const f32x16& v0, const f32x16& v1) {
+  const int lane = threadIdx.x & 63;
+  const int m = lane & 31;
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    const f32x16& v = h ? v1 : v0;
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+      const int c = h * 8 + 2 * g + (lane >> 5);
+      *(float4*)(wl + m * 64 + ((c ^ (m & 15)) * 4)) =
+          make_float4(v[4 * g], v[4 * g + 1], v[4 * g + 2], v[4 * g + 3]);
+    }
+  }
+}
+// Row lane / 2 of the staged pair, columns 32 (lane % 2) .. + 32 of the 64.
+__device__ __forceinline__ void s_unstage(const float* wl, float (&f)[32]) {
+  const int lane = threadIdx.x & 63;
+  const int rr = lane >> 1, hc = (lane & 1) * 8;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const float4 q = *(const float4*)(wl + rr * 64 + (((hc + i) ^ (rr & 15)) * 4));
+    f[4 * i] = q.x;
+    f[4 * i + 1] = q.y;
+    f[4 * i + 2] = q.z;
+    f[4 * i + 3] = q.w;
+  }
+}
+__device__ __forceinline__ void s_store16(bf16_t* o, const float* f) {
+  *(uint4*)o = make_uint4(pack2(f[0], f[1]), pack2(f[2], f[3]), pack2(f[4], f[5]), pack2(f[6], f[7]));
+  *(uint4*)(o + 8) =
+      make_uint4(pack2(f[8], f[9]), pack2(f[10], f[11]), pack2(f[12], f[13]), pack2(f[14], f[15]));
+}
+
+template <int KIND>
+__device__ __forceinline__ void s_epilogue(const Layer& L, const STile& T, f32x16 (&acc)[SFM][SFN], float* wl) {
+  static_assert(KIND != SK_DH, "dh runs on the register-path kernel");
+  const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
+  const int wm = wid / SWN, wn = wid % SWN;
+  const int rr = lane >> 1, half = lane & 1;
+  const int n = L.n, d = L.d;
+#pragma unroll
+  for (int fm = 0; fm < SFM; ++fm)
+#pragma unroll
+    for (int pr = 0; pr < SFN / 2; ++pr) {
+      s_stage_pair(wl, acc[fm][2 * pr], acc[fm][2 * pr + 1]);
+      float f[32];
+      s_unstage(wl, f);
+      const int m = wm * STM + fm * 32 + rr;
+      if (m >= T.mrows) continue;
+      const int64_t p = T.row0 + m;
+      if constexpr (KIND == SK_GU) {
+        // columns 0..31 of the pair are gate(j), 32..63 up(j), j = jb + 0..31;
+        // this lane has j = jb + 16 half + 0..15 of both
+        const int j = T.nt * (SBN / 2) + (wn * (SFN / 2) + pr) * 32 + 16 * half;
+        if (j >= n) continue;
+        float gv[16], uv[16], hv[16];
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          // lane half 0 read columns 0..31 (gate), half 1 columns 32..63 (up):
+          // swap halves with the neighbour lane so each holds gate and up of
+          // its own 16 j
+          const float lo = f[i], hi = f[16 + i];  // static indices: no select chains
+          const float mine = half ? hi : lo;
+          const float other = __shfl_xor(half ? lo : hi, 1, 64);
+          gv[i] = half ? other : mine;
+          uv[i] = half ? mine : other;
+          hv[i] = silu_f(gv[i]) * uv[i];
+        }
+        s_store16(L.g + p * 2 * n + j, gv);
+        s_store16(L.g + p * 2 * n + n + j, uv);
+        s_store16(L.h + p * n + j, hv);
+      } else {
+        const int c = T.nt * SBN + wn * STN + pr * 64 + 32 * half;
+        if (c >= d) continue;
+        s_store16(L.o + p * d + c, f);
+        s_store16(L.o + p * d + c + 16, f + 16);
+      }
+    }
+}
+
+template <int KIND>
+__global__ __launch_bounds__(SNT) __attribute__((amdgpu_waves_per_eu(1, 1))) void k_stream(const Layer L) {
+  __shared__ __attribute__((aligned(1024))) bf16_t ring[SNS * SSTAGE];
+  __shared__ __attribute__((aligned(16))) int tokbuf[2][SBM];
+  __shared__ int pre[MAX_ET + 1];
+  __shared__ int segst[MAX_ET + 1];
+  __shared__ int sh[SNW];
+  const int Et = L.Et;
+  for (int e = threadIdx.x; e <= Et; e += SNT)
+    segst[e] = e < L.E ? L.offsets[e] : e == L.E ? L.P : L.Ptot;
+  __syncthreads();
+  expert_prefix<SNT>(L, pre, sh, [&](int e) { return cdiv(segst[e + 1] - segst[e], SBM); });
+  const int ntn = s_ntn<KIND>(L);
+  const int total = pre[Et] * ntn;
+  const int G = gridDim.x;
+  int tc = first_tile();
+  if (tc >= total) return;
+  const int wid = threadIdx.x >> 6;
+  const int rs = L.rs, r = L.r;
+  const uint32_t ring_b = (uint32_t)(uintptr_t)ring;
+
+  // issue cursor on the first tile; its gather indices come in directly
+  STile ti = s_decode(pre, segst, Et, tc, ntn);
+  if (SP<KIND>::A_GATHER) {
+    for (int m = threadIdx.x; m < SBM; m += SNT)
+      tokbuf[0][m] = ti.row0 + m < L.Ptot ? L.tok[ti.row0 + m] : 0;
+    __syncthreads();
+  }
+  SIssue S;
+  s_setup<KIND>(L, ti, tokbuf[0], S);
+  int iord = 0;        // ordinal of the issue tile among this workgroup's tiles
+  bool idone = false;  // no tile left to issue: repeat the last step
+  // gather indices of the following tile, a whole tile ahead (wave 0, before
+  // the step's panels, so the step's wait covers it)
+  auto issue_tok = [&](int t_next, int slot) {
+    if (!SP<KIND>::A_GATHER || wid != 0 || t_next >= total) return;
+    const STile Tn = s_decode(pre, segst, Et, t_next, ntn);
+    const int lane = threadIdx.x & 63;
+    dma16(make_desc(L.tok + Tn.row0, (int64_t)(L.Ptot - Tn.row0) * 4), (uint32_t)lane * 16u, 0,
+          __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)&tokbuf[slot][0]));
+  };
+  issue_tok(tc + G, 1);
+  int gi = 0;  // global issue step (ring slot gi % SNS)
+  auto issue_next = [&]() {
+    if (S.step == S.stot) {
+      const int tn = ti.t + G;
+      if (!idone && tn < total) {
+        ++iord;
+        ti = s_decode(pre, segst, Et, tn, ntn);
+        s_setup<KIND>(L, ti, tokbuf[iord & 1], S);
+        issue_tok(tn + G, (iord + 1) & 1);
+      } else {
+        idone = true;
+        S.step = S.stot - 1;
+      }
+    }
+    s_issue<KIND>(S, S.step, ring_b + (uint32_t)(gi % SNS) * SSTAGE * 2, rs, r);
+    if (!idone) ++S.step;
+    ++gi;
+  };
+#pragma unroll 1
+  for (int s = 0; s < SPD; ++s) issue_next();
+
+  // compute: tiles in order, each its base steps then its rank-r steps
+  const int smain = s_kmain<KIND>(L) / SK;
+  const int slora = cdiv(rs, SK);
+  int gc = 0;
+#pragma unroll 1
+  for (; tc < total; tc += G) {
+    const STile tcur = s_decode(pre, segst, Et, tc, ntn);
+    f32x16 acc[SFM][SFN];
+#pragma unroll
+    for (int fm = 0; fm < SFM; ++fm)
+#pragma unroll
+      for (int fn = 0; fn < SFN; ++fn) acc[fm][fn] = (f32x16)(0.0f);
+#pragma unroll 1
+    for (int k = 0; k < smain; ++k) {
+      wait_vmcnt<(SPD - 1) * PER>();
+      __syncthreads();
+      issue_next();
+      const bf16_t* st = ring + (gc % SNS) * SSTAGE;
+      s_mma<SP<KIND>::B_MAIN_MN>(st, st + PANEL, acc);
+      ++gc;
+    }
+#pragma unroll 1
+    for (int k = 0; k < slora; ++k) {
+      wait_vmcnt<(SPD - 1) * PER>();
+      __syncthreads();
+      issue_next();
+      const bf16_t* st = ring + (gc % SNS) * SSTAGE;
+      s_mma<SP<KIND>::B_LORA_MN>(st, st + PANEL, acc);
+      ++gc;
+    }
+    // the stage consumed last is free until the next step's issue, once
+    // every wave is done reading it
+    __syncthreads();
+    s_epilogue<KIND>(L, tcur, acc, (float*)(ring + ((gc + SNS - 1) % SNS) * SSTAGE) + wid * 2048);
+  }
+  wait_vmcnt<0>();
+}
+
+}  // namespace
+
+template <int KIND>
+static hipError_t launch_stream(const Layer& L, hipStream_t st, const char* name) {
+  const int ntn = KIND == SK_GU ? cdiv(L.n, SBN / 2) : KIND == SK_DH ? cdiv(L.n, SBN) : cdiv(L.d, SBN);
+  const int64_t tiles = (int64_t)(L.Ptot / SBM + L.Et) * ntn;
+  int g = (int)std::min<int64_t>(tiles, L.ncu);
+  g = std::max((g + 7) & ~7, 8);
+  MOE_LAUNCH(name, k_stream<KIND>, dim3(g), dim3(SNT), 0, st, L);
+  return hipGetLastError();
+}
+
+hipError_t stream_gate_up(const Layer& L, hipStream_t st) { return launch_stream<SK_GU>(L, st, "gate_up"); }
+hipError_t stream_down(const Layer& L, hipStream_t st) { return launch_stream<SK_DN>(L, st, "down"); }
+hipError_t stream_dx(const Layer& L, hipStream_t st) { return launch_stream<SK_DX>(L, st, "dx"); }
+
+}  // namespace moe
