@@ -53,6 +53,8 @@ static_assert(NI * SNW * 1024 == PANEL * 2, "panel split");
 
 enum StreamKind { SK_GU = 0, SK_DN = 1, SK_DH = 2, SK_DX = 3 };
 
+typedef unsigned v4u __attribute__((ext_vector_type(4)));
+
 typedef short v4s __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) v4s lds_v4s;
 
@@ -332,10 +334,38 @@ __device__ __forceinline__ void s_unstage(const float* wl, float (&f)[32]) {
     f[4 * i + 3] = q.w;
   }
 }
-__device__ __forceinline__ void s_store16(bf16_t* o, const float* f) {
-  *(uint4*)o = make_uint4(pack2(f[0], f[1]), pack2(f[2], f[3]), pack2(f[4], f[5]), pack2(f[6], f[7]));
-  *(uint4*)(o + 8) =
-      make_uint4(pack2(f[8], f[9]), pack2(f[10], f[11]), pack2(f[12], f[13]), pack2(f[14], f[15]));
+// 16 bf16 values at byte voff of the buffer: exactly two store instructions,
+// also for padding rows (voff out of range: the stores are dropped), so
+// every wave issues the same known number of stores per tile.
+// Row lane / 8 + 8 i (i = 0..3) of the staged pair, columns 8 (lane % 8)
+// .. + 8: each store instruction then writes 8 whole 128-byte row segments.
+__device__ __forceinline__ void s_unstage_rows(const float* wl, int i, float (&f)[8]) {
+  const int lane = threadIdx.x & 63;
+  const int r = (lane >> 3) + 8 * i, c = (lane & 7) * 2;
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    const float4 q = *(const float4*)(wl + r * 64 + (((c + h) ^ (r & 15)) * 4));
+    f[4 * h] = q.x;
+    f[4 * h + 1] = q.y;
+    f[4 * h + 2] = q.z;
+    f[4 * h + 3] = q.w;
+  }
+}
+__device__ __forceinline__ void s_store8(rsrc_t r, uint32_t voff, const float* f) {
+  const v4u a = {pack2(f[0], f[1]), pack2(f[2], f[3]), pack2(f[4], f[5]), pack2(f[6], f[7])};
+  __builtin_amdgcn_raw_buffer_store_b128(a, r, voff, 0, 0);
+}
+__device__ __forceinline__ void s_store16(rsrc_t r, uint32_t voff, const float* f) {
+  const v4u a = {pack2(f[0], f[1]), pack2(f[2], f[3]), pack2(f[4], f[5]), pack2(f[6], f[7])};
+  const v4u b = {pack2(f[8], f[9]), pack2(f[10], f[11]), pack2(f[12], f[13]), pack2(f[14], f[15])};
+  __builtin_amdgcn_raw_buffer_store_b128(a, r, voff, 0, 0);
+  __builtin_amdgcn_raw_buffer_store_b128(b, r, voff + 16u, 0, 0);
+}
+
+// Store instructions each wave issues in one tile's epilogue.
+template <int KIND>
+constexpr int s_epi_stores() {
+  return SFM * (SFN / 2) * (KIND == SK_GU ? 6 : 4);  // GU: 3 x 2 per lane; else 4 rows
 }
 
 template <int KIND>
@@ -345,27 +375,37 @@ __device__ __forceinline__ void s_epilogue(const Layer& L, const STile& T, f32x1
   const int wm = wid / SWN, wn = wid % SWN;
   const int rr = lane >> 1, half = lane & 1;
   const int n = L.n, d = L.d;
+  const int64_t P = L.Ptot;
+  const rsrc_t rg = make_rsrc(L.g, P * 2 * n * 2), rh = make_rsrc(L.h, P * n * 2), ro = make_rsrc(L.o, P * d * 2);
 #pragma unroll
   for (int fm = 0; fm < SFM; ++fm)
 #pragma unroll
     for (int pr = 0; pr < SFN / 2; ++pr) {
       s_stage_pair(wl, acc[fm][2 * pr], acc[fm][2 * pr + 1]);
+      if constexpr (KIND != SK_GU) {
+        const int c = T.nt * SBN + wn * STN + pr * 64 + (lane & 7) * 8;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          float f8[8];
+          s_unstage_rows(wl, i, f8);
+          const int m = wm * STM + fm * 32 + (lane >> 3) + 8 * i;
+          const bool ok = m < T.mrows && c < d;
+          s_store8(ro, ok ? (uint32_t)(((int64_t)(T.row0 + m) * d + c) * 2) : OOB, f8);
+        }
+        continue;
+      }
       float f[32];
       s_unstage(wl, f);
       const int m = wm * STM + fm * 32 + rr;
-      if (m >= T.mrows) continue;
       const int64_t p = T.row0 + m;
       if constexpr (KIND == SK_GU) {
         // columns 0..31 of the pair are gate(j), 32..63 up(j), j = jb + 0..31;
-        // this lane has j = jb + 16 half + 0..15 of both
+        // the two lanes of a row split j = jb + 16 half + 0..15
         const int j = T.nt * (SBN / 2) + (wn * (SFN / 2) + pr) * 32 + 16 * half;
-        if (j >= n) continue;
+        const bool ok = m < T.mrows && j < n;
         float gv[16], uv[16], hv[16];
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
-          // lane half 0 read columns 0..31 (gate), half 1 columns 32..63 (up):
-          // swap halves with the neighbour lane so each holds gate and up of
-          // its own 16 j
           const float lo = f[i], hi = f[16 + i];  // static indices: no select chains
           const float mine = half ? hi : lo;
           const float other = __shfl_xor(half ? lo : hi, 1, 64);
@@ -373,14 +413,18 @@ __device__ __forceinline__ void s_epilogue(const Layer& L, const STile& T, f32x1
           uv[i] = half ? mine : other;
           hv[i] = silu_f(gv[i]) * uv[i];
         }
-        s_store16(L.g + p * 2 * n + j, gv);
-        s_store16(L.g + p * 2 * n + n + j, uv);
-        s_store16(L.h + p * n + j, hv);
+        const uint32_t og = ok ? (uint32_t)((p * 2 * n + j) * 2) : OOB;
+        const uint32_t ou = ok ? (uint32_t)((p * 2 * n + n + j) * 2) : OOB;
+        const uint32_t oh = ok ? (uint32_t)((p * n + j) * 2) : OOB;
+        s_store16(rg, og, gv);
+        s_store16(rg, ou, uv);
+        s_store16(rh, oh, hv);
       } else {
         const int c = T.nt * SBN + wn * STN + pr * 64 + 32 * half;
-        if (c >= d) continue;
-        s_store16(L.o + p * d + c, f);
-        s_store16(L.o + p * d + c + 16, f + 16);
+        const bool ok = m < T.mrows && c < d;
+        const uint32_t oo = ok ? (uint32_t)((p * d + c) * 2) : OOB;
+        s_store16(ro, oo, f);
+        s_store16(ro, ok ? oo + 32u : OOB, f + 16);
       }
     }
 }
@@ -452,6 +496,18 @@ __global__ __launch_bounds__(SNT) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
   const int smain = s_kmain<KIND>(L) / SK;
   const int slora = cdiv(rs, SK);
   int gc = 0;
+  // Ring wait before step c of a tile: the stage issued SPD steps earlier
+  // must be in; younger than it are the SPD - 1 later stages and, in the
+  // first SPD steps of every tile but the first, the previous tile's
+  // epilogue stores (issued after this tile's first stages; vector memory
+  // operations retire in issue order, so counting them is exact).
+  constexpr int WAIT = (SPD - 1) * PER;
+  constexpr int WAIT_EPI = WAIT + s_epi_stores<KIND>() < 63 ? WAIT + s_epi_stores<KIND>() : 63;
+  bool after_epi = false;
+  auto ring_wait = [&](int c) {
+    if (after_epi && c < SPD) wait_vmcnt<WAIT_EPI>();
+    else wait_vmcnt<WAIT>();
+  };
 #pragma unroll 1
   for (; tc < total; tc += G) {
     const STile tcur = s_decode(pre, segst, Et, tc, ntn);
@@ -462,7 +518,7 @@ __global__ __launch_bounds__(SNT) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
       for (int fn = 0; fn < SFN; ++fn) acc[fm][fn] = (f32x16)(0.0f);
 #pragma unroll 1
     for (int k = 0; k < smain; ++k) {
-      wait_vmcnt<(SPD - 1) * PER>();
+      ring_wait(k);
       __syncthreads();
       issue_next();
       const bf16_t* st = ring + (gc % SNS) * SSTAGE;
@@ -471,7 +527,7 @@ __global__ __launch_bounds__(SNT) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
     }
 #pragma unroll 1
     for (int k = 0; k < slora; ++k) {
-      wait_vmcnt<(SPD - 1) * PER>();
+      ring_wait(smain + k);
       __syncthreads();
       issue_next();
       const bf16_t* st = ring + (gc % SNS) * SSTAGE;
@@ -482,6 +538,7 @@ __global__ __launch_bounds__(SNT) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
     // every wave is done reading it
     __syncthreads();
     s_epilogue<KIND>(L, tcur, acc, (float*)(ring + ((gc + SNS - 1) % SNS) * SSTAGE) + wid * 2048);
+    after_epi = true;
   }
   wait_vmcnt<0>();
 }
