@@ -253,9 +253,12 @@ __device__ __forceinline__ void s_issue(const SIssue& S, int step, uint32_t sb, 
   }
 }
 
-// MFMAs of one ring stage, k = 32: the wave's 4 x 4 fragments.  (Padding rows
-// are multiplied too: branching around fragments splits the accumulator's
-// live range and the register allocator then copies it through memory.)
+// MFMAs of one ring stage, k = 32: the wave's 4 x 4 fragments.  All fragment
+// reads of the stage are issued first (64 VGPRs), then the 32 MFMAs, so the
+// second half's reads land under the first half's MFMAs and LDS latency is
+// exposed once per stage.  (Padding rows are multiplied too: branching around
+// fragments splits the accumulator's live range and the register allocator
+// then copies it through memory.)
 template <bool BMN>
 __device__ __forceinline__ void s_mma(const bf16_t* As, const bf16_t* Bs, f32x16 (&acc)[SFM][SFN]) {
   const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
@@ -267,16 +270,16 @@ __device__ __forceinline__ void s_mma(const bf16_t* As, const bf16_t* Bs, f32x16
   // read) at columns 16 (g & 1) + 4 rr of the fragment; the transposing read
   // gives lane (g, j) the 4 k values of column 16 (g & 1) + j.
   const int g = lane >> 4, q = (lane >> 2) & 3, rr = lane & 3;
+  uint4 a[SK / 16][SFM], b[SK / 16][SFN];
 #pragma unroll
   for (int kk = 0; kk < SK / 16; ++kk) {
     const int c = ((kk * 2 + (lane >> 5)) ^ swz) * 16;
-    uint4 a[SFM], b[SFN];
 #pragma unroll
-    for (int fm = 0; fm < SFM; ++fm) a[fm] = *(const uint4*)(ab + fm * 32 * (SK * 2) + c);
+    for (int fm = 0; fm < SFM; ++fm) a[kk][fm] = *(const uint4*)(ab + fm * 32 * (SK * 2) + c);
     if constexpr (!BMN) {
       const char* bb = (const char*)Bs + (wn * STN + l) * (SK * 2);
 #pragma unroll
-      for (int fn = 0; fn < SFN; ++fn) b[fn] = *(const uint4*)(bb + fn * 32 * (SK * 2) + c);
+      for (int fn = 0; fn < SFN; ++fn) b[kk][fn] = *(const uint4*)(bb + fn * 32 * (SK * 2) + c);
     } else {
       const int krow = kk * 16 + 8 * (g >> 1) + q;
       const int kx = (krow & 3) * 4;
@@ -286,17 +289,23 @@ __device__ __forceinline__ void s_mma(const bf16_t* As, const bf16_t* Bs, f32x16
         const char* p = (const char*)Bs + krow * (SBN * 2) + (((col >> 3) ^ kx) * 16) + (col & 7) * 2;
         const v4s lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s*)p);
         const v4s hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s*)(p + 4 * SBN * 2));
-        b[fn] = make_uint4((uint32_t)(uint16_t)lo[0] | ((uint32_t)(uint16_t)lo[1] << 16),
-                           (uint32_t)(uint16_t)lo[2] | ((uint32_t)(uint16_t)lo[3] << 16),
-                           (uint32_t)(uint16_t)hi[0] | ((uint32_t)(uint16_t)hi[1] << 16),
-                           (uint32_t)(uint16_t)hi[2] | ((uint32_t)(uint16_t)hi[3] << 16));
+        b[kk][fn] = make_uint4((uint32_t)(uint16_t)lo[0] | ((uint32_t)(uint16_t)lo[1] << 16),
+                               (uint32_t)(uint16_t)lo[2] | ((uint32_t)(uint16_t)lo[3] << 16),
+                               (uint32_t)(uint16_t)hi[0] | ((uint32_t)(uint16_t)hi[1] << 16),
+                               (uint32_t)(uint16_t)hi[2] | ((uint32_t)(uint16_t)hi[3] << 16));
       }
     }
+  }
+#pragma unroll
+  for (int kk = 0; kk < SK / 16; ++kk)
 #pragma unroll
     for (int fm = 0; fm < SFM; ++fm)
 #pragma unroll
-      for (int fn = 0; fn < SFN; ++fn) acc[fm][fn] = mfma32(b[fn], a[fm], acc[fm][fn]);
-  }
+      for (int fn = 0; fn < SFN; ++fn) acc[fm][fn] = mfma32(b[kk][fn], a[kk][fm], acc[fm][fn]);
+  // keep that order: every LDS read of the stage, then the MFMAs
+  constexpr int NREAD = (SK / 16) * (SFM + (BMN ? 2 : 1) * SFN);
+  __builtin_amdgcn_sched_group_barrier(0x100, NREAD, 0);
+  __builtin_amdgcn_sched_group_barrier(0x008, (SK / 16) * SFM * SFN, 0);
 }
 
 // Epilogue, through LDS.  The accumulators stay in AGPRs until they are
