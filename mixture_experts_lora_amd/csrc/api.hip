@@ -88,6 +88,8 @@ void attach_common(Layer& L, const moe_routing* rt, const moe_weights* w, const 
   L.dg = (bf16_t*)(base + wl.dg);
   L.qdn = (bf16_t*)(base + wl.qdn);
   L.qgu = (bf16_t*)(base + wl.qgu);
+  L.hw = (bf16_t*)(base + wl.hw);
+  L.qw = (bf16_t*)(base + wl.qw);
   L.partial = (float*)(base + wl.partial);
   L.pre_partial = (float*)(base + wl.pre_partial);
   for (int i = 0; i < 4; ++i) L.partial_off[i] = wl.partial_off[i];

@@ -1170,12 +1170,42 @@ static void launch_grad(const Layer& L, hipStream_t st, const char* name) {
              0, st, L);
 }
 
+// LoRA-gradient tiles for rank <= 64: M = r (dB) or N = r (dA).
+template <int I> struct GradCfgB;
+template <> struct GradCfgB<0> { using type = Cfg<64, 128, 2, 2>; };
+template <> struct GradCfgB<1> { using type = Cfg<64, 256, 1, 4>; };
+template <> struct GradCfgB<2> { using type = Cfg<64, 256, 2, 4>; };
+template <> struct GradCfgB<3> { using type = Cfg<64, 128, 1, 2, 2, 0, 64, 2>; };
+template <> struct GradCfgB<4> { using type = Cfg<64, 128, 2, 2, 1>; };
+template <int I> struct GradCfgA;
+template <> struct GradCfgA<0> { using type = Cfg<128, 64, 4, 1>; };
+template <> struct GradCfgA<1> { using type = Cfg<256, 64, 4, 1>; };
+template <> struct GradCfgA<2> { using type = Cfg<256, 64, 4, 2>; };
+template <> struct GradCfgA<3> { using type = Cfg<128, 64, 2, 1, 2, 0, 64, 2>; };
+template <> struct GradCfgA<4> { using type = Cfg<128, 64, 4, 1, 1>; };
+#ifndef MOE_GRAD_B
+#define MOE_GRAD_B 0
+#endif
+#ifndef MOE_GRAD_A
+#define MOE_GRAD_A 0
+#endif
+
+// 1: rank <= 64 gradients on the LDS-DMA kernels of grads.hip
+#ifndef MOE_DMA_GRADS
+#define MOE_DMA_GRADS 1
+#endif
+
 hipError_t gemm_lora_grads(const Layer& L, hipStream_t st) {
-  if (L.rs <= 64) {
-    launch_grad<Cfg<64, 128, 2, 2>, GR_DB_DN>(L, st, "grad_db_dn");
-    launch_grad<Cfg<128, 64, 4, 1>, GR_DA_DN>(L, st, "grad_da_dn");
-    launch_grad<Cfg<64, 128, 2, 2>, GR_DB_GU>(L, st, "grad_db_gu");
-    launch_grad<Cfg<128, 64, 4, 1>, GR_DA_GU>(L, st, "grad_da_gu");
+  if (MOE_DMA_GRADS && L.rs <= 64) {
+    const hipError_t e = dma_lora_grads(L, st);
+    if (e != hipSuccess) return e;
+  } else if (L.rs <= 64) {
+    using CB = GradCfgB<MOE_GRAD_B>::type;
+    using CA = GradCfgA<MOE_GRAD_A>::type;
+    launch_grad<CB, GR_DB_DN>(L, st, "grad_db_dn");
+    launch_grad<CA, GR_DA_DN>(L, st, "grad_da_dn");
+    launch_grad<CB, GR_DB_GU>(L, st, "grad_db_gu");
+    launch_grad<CA, GR_DA_GU>(L, st, "grad_da_gu");
   } else {
     launch_grad<Cfg<128, 128, 2, 2>, GR_DB_DN>(L, st, "grad_db_dn");
     launch_grad<Cfg<128, 128, 2, 2>, GR_DA_DN>(L, st, "grad_da_dn");

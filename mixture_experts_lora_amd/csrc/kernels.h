@@ -44,6 +44,8 @@ struct Layer {
   bf16_t* dg;        // [Ptot, 2n]
   bf16_t* qdn;       // [Ptot, rs]
   bf16_t* qgu;       // [Ptot, rs]
+  bf16_t* hw;        // [Ptot, rs]  w * s H A_dn (dB_dn operand)
+  bf16_t* qw;        // [Ptot, rs]  w * Q_dn (dA_dn operand)
   bf16_t* y;         // [T, d]
   bf16_t* dx;        // [T, d]
   float* da_gu;      // [Et, d, r]
@@ -66,7 +68,7 @@ __host__ __device__ inline void grad_shape(int kind, int d, int n, int r, int& M
 
 // Workspace carving shared by the size query and the launchers.
 struct WsLayout {
-  size_t o, dg, qdn, qgu, partial, pre_partial, a_gu_pack, a_dn_pack, total;
+  size_t o, dg, qdn, qgu, hw, qw, partial, pre_partial, a_gu_pack, a_dn_pack, total;
   int64_t partial_off[4];
 };
 struct SavedLayout {
@@ -89,7 +91,9 @@ hipError_t gemm_gate_up(const Layer& L, hipStream_t st);   // G, H  (+ X A_gu pr
 hipError_t gemm_down(const Layer& L, hipStream_t st);      // O     (+ H A_dn pre-pass)
 hipError_t gemm_dh(const Layer& L, hipStream_t st);        // dG    (+ dO B_dn^T pre-pass)
 hipError_t gemm_dx(const Layer& L, hipStream_t st);        // dX per pair (+ dG B_gu^T)
-hipError_t gemm_lora_grads(const Layer& L, hipStream_t st);  // dA, dB of both modules
+hipError_t gemm_lora_grads(const Layer& L, hipStream_t st);
+// LDS-DMA LoRA gradients (grads.hip), rank <= 64, before the split-K reduce.
+hipError_t dma_lora_grads(const Layer& L, hipStream_t st);  // dA, dB of both modules
 
 // Element-wise / gather kernels (layer.hip).
 hipError_t launch_pack_a(const Layer& L, const bf16_t* a_gu_src, const bf16_t* a_dn_src,

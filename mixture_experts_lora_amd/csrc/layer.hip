@@ -20,6 +20,8 @@ WsLayout ws_layout(int64_t T, int d, int n, int E, int k, int r, int S) {
   w.dg = off;       off += align256((size_t)Ptot * 2 * n * 2);
   w.qdn = off;      off += align256((size_t)Ptot * rs * 2);
   w.qgu = off;      off += align256((size_t)Ptot * rs * 2);
+  w.hw = off;       off += align256((size_t)Ptot * rs * 2);
+  w.qw = off;       off += align256((size_t)Ptot * rs * 2);
   const int64_t slots = Ptot / SPLITK_ROWS + Et;
   int64_t pf = 0;
   for (int kind = 0; kind < 4; ++kind) {
