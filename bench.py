@@ -30,6 +30,7 @@ PEAK_BF16 = 2516.6e12   # MI355X dense bf16 MFMA, FLOP/s
 PEAK_HBM = 8.0e12       # MI355X HBM3E, B/s
 GEMM_KERNELS = ("gate_up", "down", "dh", "dx", "prepass_xa", "prepass_ha", "prepass_qdn",
                 "prepass_qgu", "grad_db_dn", "grad_da_dn", "grad_db_gu", "grad_da_gu")
+# per-kernel algorithmic work is per launch; the timer reports per-launch averages
 
 
 def kernel_work(c):
@@ -47,7 +48,10 @@ def kernel_work(c):
     X = T * d * b
     G, H, R, O = P * 2 * n * b, P * n * b, P * r * b, P * d * b
     idx = P * 4 * 2
+    logits = c.T * c.E * 4
+    route_out = c.T * c.k * 4 * 2 + c.E * 4 + (c.E + 1) * 4 + P * 4 * 2
     return {
+        "route": (0, logits + route_out),
         "prepass_xa": (2 * P * d * r, X + A_gu + R + idx),
         "gate_up": (2 * P * d * 2 * n + 2 * P * r * 2 * n, W_gu + B_gu + X + R + G + H + idx),
         "prepass_ha": (2 * P * n * r, H + A_dn + R),
@@ -225,6 +229,17 @@ def main():
     roof["algorithmic_flops"] = f
     roof["mfma_frac"] = f / t_dom / PEAK_BF16
 
+    # routing (all its launches) and the two combines against the HBM peak
+    mem = {}
+    route_us = sum(avg_us.get(k, 0.0) for k in ("route_topk_hist", "route_scan_blocks", "route_permute"))
+    if route_us > 0:
+        mem["route"] = {"us": round(route_us, 2), "GB/s": round(work["route"][1] / route_us / 1e3, 1)}
+    for k in ("combine_y", "combine_dx"):
+        if k in avg_us:
+            mem[k] = {"us": round(avg_us[k], 2), "GB/s": round(work[k][1] / avg_us[k] / 1e3, 1)}
+    for v in mem.values():
+        v["frac_of_hbm_peak"] = round(v["GB/s"] * 1e9 / PEAK_HBM, 3)
+
     out = {
         "metric": METRIC,
         "value": c.T / (ms * 1e-3),
@@ -245,6 +260,7 @@ def main():
         "gemm_tflops": gemm_flops / gemm_time / 1e12,
         "roofline": roof,
         "kernels_us": {k: round(v, 2) for k, v in sorted(avg_us.items())},
+        "memory_bound_kernels": mem,
     }
     if args.cpu_budget > 0:
         out["cpu_baseline"] = cpu_baseline(c, inp, args.cpu_budget)

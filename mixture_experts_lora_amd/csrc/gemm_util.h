@@ -50,9 +50,12 @@ __device__ __forceinline__ int4v make_desc(const void* base, int64_t bytes) {
 #pragma clang diagnostic push
 #pragma clang diagnostic ignored "-Winline-asm"
 __device__ __forceinline__ void dma16(int4v desc, uint32_t voff, uint32_t soff, uint32_t lds_addr) {
+  // the scalar operands are wave-uniform by contract; readfirstlane keeps the
+  // compiler from handing a VGPR copy of one to an "s" constraint
   asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, %3 offen lds"
                :
-               : "s"(lds_addr), "v"(voff), "s"(desc), "s"(soff)
+               : "s"(__builtin_amdgcn_readfirstlane(lds_addr)), "v"(voff), "s"(desc),
+                 "s"(__builtin_amdgcn_readfirstlane(soff))
                : "memory", "m0");
 }
 #pragma clang diagnostic pop

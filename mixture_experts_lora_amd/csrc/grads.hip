@@ -138,11 +138,13 @@ __global__ __launch_bounds__(GNT) __attribute__((amdgpu_waves_per_eu(2))) void k
     const int slot = t / per_slot;
     const int rem = t - slot * per_slot;
     const int nt = rem / nmt, mt = rem - nt * nmt;
-    const int e = find_expert(pre, L.Et, slot, 1);
-    const int chunk = slot - pre[e];
-    const int nchunk = pre[e + 1] - pre[e];
-    const int kb = seg_start(L, e) + chunk * SPLITK_ROWS;
-    const int kn = min(seg_count(L, e) - chunk * SPLITK_ROWS, SPLITK_ROWS);
+    // tile scalars are wave-uniform: keep them in scalar registers (the DMA
+    // descriptors built from them must be)
+    const int e = __builtin_amdgcn_readfirstlane(find_expert(pre, L.Et, slot, 1));
+    const int chunk = __builtin_amdgcn_readfirstlane(slot - pre[e]);
+    const int nchunk = __builtin_amdgcn_readfirstlane(pre[e + 1] - pre[e]);
+    const int kb = __builtin_amdgcn_readfirstlane(seg_start(L, e) + chunk * SPLITK_ROWS);
+    const int kn = __builtin_amdgcn_readfirstlane(min(seg_count(L, e) - chunk * SPLITK_ROWS, SPLITK_ROWS));
     const int m0 = mt * P::BM, c0 = nt * P::BN;
     if (P::U_GATHER || P::V_GATHER) {
       for (int i = threadIdx.x; i < kn; i += GNT) tokbuf[i] = L.tok[kb + i];

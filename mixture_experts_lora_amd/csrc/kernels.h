@@ -91,9 +91,9 @@ hipError_t gemm_gate_up(const Layer& L, hipStream_t st);   // G, H  (+ X A_gu pr
 hipError_t gemm_down(const Layer& L, hipStream_t st);      // O     (+ H A_dn pre-pass)
 hipError_t gemm_dh(const Layer& L, hipStream_t st);        // dG    (+ dO B_dn^T pre-pass)
 hipError_t gemm_dx(const Layer& L, hipStream_t st);        // dX per pair (+ dG B_gu^T)
-hipError_t gemm_lora_grads(const Layer& L, hipStream_t st);
+hipError_t gemm_lora_grads(const Layer& L, hipStream_t st);  // dA, dB of both modules
 // LDS-DMA LoRA gradients (grads.hip), rank <= 64, before the split-K reduce.
-hipError_t dma_lora_grads(const Layer& L, hipStream_t st);  // dA, dB of both modules
+hipError_t dma_lora_grads(const Layer& L, hipStream_t st);
 
 // Element-wise / gather kernels (layer.hip).
 hipError_t launch_pack_a(const Layer& L, const bf16_t* a_gu_src, const bf16_t* a_dn_src,
