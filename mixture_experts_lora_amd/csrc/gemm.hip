@@ -607,6 +607,9 @@ template <> struct MainCfg<27> { using type = Cfg<256, 256, 4, 2, 0, 4, 32>; }; 
 #ifndef MOE_STREAM_DX
 #define MOE_STREAM_DX 1
 #endif
+#ifndef MOE_STREAM_DH
+#define MOE_STREAM_DH 1
+#endif
 #ifndef MOE_CFG_GU
 #define MOE_CFG_GU 7
 #endif
@@ -1146,6 +1149,7 @@ hipError_t gemm_down(const Layer& L, hipStream_t st) {
 hipError_t gemm_dh(const Layer& L, hipStream_t st) {
   using C = MainCfg<MOE_CFG_DH>::type;
   launch_prepass<PRE_QDN>(L, st, "prepass_qdn");
+  if (MOE_STREAM_DH) return stream_dh(L, st);
   const int tiles = mtiles_bound(L, C::BM) * cdiv(L.n, C::BN);
   MOE_LAUNCH("dh", k_dh<C>, dim3(grid_for(tiles, wg_per_cu<C>(), L.ncu)), dim3(C::NT), 0, st, L);
   return hipGetLastError();

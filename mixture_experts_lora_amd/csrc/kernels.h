@@ -87,6 +87,7 @@ hipError_t launch_route(const float* logits, int64_t T, int E, int k, int32_t* i
 hipError_t stream_gate_up(const Layer& L, hipStream_t st);
 hipError_t stream_down(const Layer& L, hipStream_t st);
 hipError_t stream_dx(const Layer& L, hipStream_t st);
+hipError_t stream_dh(const Layer& L, hipStream_t st);
 hipError_t gemm_gate_up(const Layer& L, hipStream_t st);   // G, H  (+ X A_gu pre-pass)
 hipError_t gemm_down(const Layer& L, hipStream_t st);      // O     (+ H A_dn pre-pass)
 hipError_t gemm_dh(const Layer& L, hipStream_t st);        // dG    (+ dO B_dn^T pre-pass)

@@ -371,15 +371,88 @@ __device__ __forceinline__ void s_store16(rsrc_t r, uint32_t voff, const float* 
   __builtin_amdgcn_raw_buffer_store_b128(b, r, voff + 16u, 0, 0);
 }
 
+// dh epilogue: dH (without the routing weight) of fragment pair (fm, pr) is
+// staged as above and read back by rows: lane -> row (lane / 8) + 8 i,
+// j = jb + 8 (lane % 8) + 0..7.  The SwiGLU backward needs gate and up of the
+// same (row, j) from the saved G: those loads run one fragment pair ahead
+// (the first one's wait also covers the next tile's panels already in
+// flight; after that they overlap the previous pair's math and stores).
+struct GUq {
+  uint4 g[4], u[4];
+  float w[4];
+};
+__device__ __forceinline__ void s_dh_load(const Layer& L, const STile& T, rsrc_t rg, rsrc_t rw, int q,
+                                          GUq& o) {
+  const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
+  const int wm = wid / SWN, wn = wid % SWN;
+  const int fm = q / (SFN / 2), pr = q % (SFN / 2);
+  const int n = L.n;
+  const int j = T.nt * SBN + wn * STN + pr * 64 + (lane & 7) * 8;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int m = wm * STM + fm * 32 + (lane >> 3) + 8 * i;
+    const bool ok = m < T.mrows && j < n;
+    const uint32_t og = ok ? (uint32_t)(((int64_t)(T.row0 + m) * 2 * n + j) * 2) : OOB;
+    const auto gq = __builtin_amdgcn_raw_buffer_load_b128(rg, og, 0, 0);
+    const auto uq = __builtin_amdgcn_raw_buffer_load_b128(rg, ok ? og + (uint32_t)(n * 2) : OOB, 0, 0);
+    o.g[i] = make_uint4(gq[0], gq[1], gq[2], gq[3]);
+    o.u[i] = make_uint4(uq[0], uq[1], uq[2], uq[3]);
+    o.w[i] = __uint_as_float((uint32_t)__builtin_amdgcn_raw_buffer_load_b32(rw, ok ? (uint32_t)(T.row0 + m) * 4u : OOB, 0, 0));
+  }
+}
+__device__ __forceinline__ void s_epilogue_dh(const Layer& L, const STile& T, f32x16 (&acc)[SFM][SFN], float* wl) {
+  const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
+  const int wm = wid / SWN, wn = wid % SWN;
+  const int n = L.n;
+  const int64_t P = L.Ptot;
+  const rsrc_t rg = make_rsrc(L.g, P * 2 * n * 2), rdg = make_rsrc(L.dg, P * 2 * n * 2);
+  const rsrc_t rw = make_rsrc(L.wgt, P * 4);
+  GUq cur, nxt;
+  s_dh_load(L, T, rg, rw, 0, cur);
+#pragma unroll
+  for (int q = 0; q < SFM * (SFN / 2); ++q) {
+    const int fm = q / (SFN / 2), pr = q % (SFN / 2);
+    if (q + 1 < SFM * (SFN / 2)) s_dh_load(L, T, rg, rw, q + 1, nxt);
+    s_stage_pair(wl, acc[fm][2 * pr], acc[fm][2 * pr + 1]);
+    const int j = T.nt * SBN + wn * STN + pr * 64 + (lane & 7) * 8;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      float f8[8];
+      s_unstage_rows(wl, i, f8);
+      const int m = wm * STM + fm * 32 + (lane >> 3) + 8 * i;
+      const bool ok = m < T.mrows && j < n;
+      const int64_t p = T.row0 + m;
+      const uint32_t og = ok ? (uint32_t)((p * 2 * n + j) * 2) : OOB;
+      const float w = cur.w[i];
+      const uint32_t gw[4] = {cur.g[i].x, cur.g[i].y, cur.g[i].z, cur.g[i].w};
+      const uint32_t uw[4] = {cur.u[i].x, cur.u[i].y, cur.u[i].z, cur.u[i].w};
+      float dgt[8], dup[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const float gv = bf2f((bf16_t)((e & 1) ? gw[e >> 1] >> 16 : gw[e >> 1] & 0xffffu));
+        const float uv = bf2f((bf16_t)((e & 1) ? uw[e >> 1] >> 16 : uw[e >> 1] & 0xffffu));
+        const float dh = w * f8[e];
+        const float sg = sigmoid_f(gv);
+        dgt[e] = dh * uv * (sg * (1.0f + gv * (1.0f - sg)));
+        dup[e] = dh * (gv * sg);
+      }
+      s_store8(rdg, og, dgt);
+      s_store8(rdg, ok ? og + (uint32_t)(n * 2) : OOB, dup);
+    }
+    if (q + 1 < SFM * (SFN / 2)) cur = nxt;
+  }
+}
+
 // Store instructions each wave issues in one tile's epilogue.
 template <int KIND>
 constexpr int s_epi_stores() {
-  return SFM * (SFN / 2) * (KIND == SK_GU ? 6 : 4);  // GU: 3 x 2 per lane; else 4 rows
+  // per fragment pair: GU 3 outputs x 2; DH 4 rows x (dgate, dup); else 4 rows
+  return SFM * (SFN / 2) * (KIND == SK_GU ? 6 : KIND == SK_DH ? 8 : 4);
 }
 
 template <int KIND>
 __device__ __forceinline__ void s_epilogue(const Layer& L, const STile& T, f32x16 (&acc)[SFM][SFN], float* wl) {
-  static_assert(KIND != SK_DH, "dh runs on the register-path kernel");
+  static_assert(KIND != SK_DH, "dh has its own epilogue");
   const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
   const int wm = wid / SWN, wn = wid % SWN;
   const int rr = lane >> 1, half = lane & 1;
@@ -546,7 +619,10 @@ __global__ __launch_bounds__(SNT) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
     // the stage consumed last is free until the next step's issue, once
     // every wave is done reading it
     __syncthreads();
-    s_epilogue<KIND>(L, tcur, acc, (float*)(ring + ((gc + SNS - 1) % SNS) * SSTAGE) + wid * 2048);
+    if constexpr (KIND == SK_DH)
+      s_epilogue_dh(L, tcur, acc, (float*)(ring + ((gc + SNS - 1) % SNS) * SSTAGE) + wid * 2048);
+    else
+      s_epilogue<KIND>(L, tcur, acc, (float*)(ring + ((gc + SNS - 1) % SNS) * SSTAGE) + wid * 2048);
     after_epi = true;
   }
   wait_vmcnt<0>();
@@ -567,5 +643,6 @@ static hipError_t launch_stream(const Layer& L, hipStream_t st, const char* name
 hipError_t stream_gate_up(const Layer& L, hipStream_t st) { return launch_stream<SK_GU>(L, st, "gate_up"); }
 hipError_t stream_down(const Layer& L, hipStream_t st) { return launch_stream<SK_DN>(L, st, "down"); }
 hipError_t stream_dx(const Layer& L, hipStream_t st) { return launch_stream<SK_DX>(L, st, "dx"); }
+hipError_t stream_dh(const Layer& L, hipStream_t st) { return launch_stream<SK_DH>(L, st, "dh"); }
 
 }  // namespace moe
