@@ -782,7 +782,6 @@ __global__ __launch_bounds__(C::NT) __attribute__((amdgpu_waves_per_eu(C::OCC)))
 // factor (B_dn, B_gu: out = act . F^T), and act is X[token], H, dY[token]
 // (without the routing weight) or dG.  Columns in [r, rs) come out zero.
 // Every consumer of these rank-r rows takes the LoRA scale from them.
-enum PrepassKind { PRE_XA = 0, PRE_HA = 1, PRE_QDN = 2, PRE_QGU = 3 };
 
 // The contraction (d, n or 2n) can be split over `nsplit` workgroups per row
 // tile: each writes an fp32 partial [split][Ptot][rs] that k_prepass_reduce
@@ -1107,8 +1106,16 @@ static int grid_for(int max_tiles, int per_cu, int ncu) {
 
 static int mtiles_bound(const Layer& L, int BM) { return L.Ptot / BM + L.Et; }
 
+#ifndef MOE_STREAM_PRE
+#define MOE_STREAM_PRE 1
+#endif
+
 template <int KIND>
 static void launch_prepass(const Layer& L, hipStream_t st, const char* name) {
+  if (MOE_STREAM_PRE && L.rs <= 64) {
+    stream_prepass(L, KIND, st);
+    return;
+  }
   const int mt = mtiles_bound(L, 128);
   const int K = KIND == PRE_XA || KIND == PRE_QDN ? L.d : KIND == PRE_HA ? L.n : 2 * L.n;
   const int nsplit = prepass_splits(L.Ptot, L.Et, K, L.ncu);

@@ -84,6 +84,10 @@ hipError_t launch_route(const float* logits, int64_t T, int E, int k, int32_t* i
 
 // Grouped GEMM launchers (gemm.hip).
 // Streamed main GEMMs (stream.hip): the product only, without the pre-pass.
+// Rank-r pre-passes (s X A_gu, s H A_dn, s dY B_dn^T, s dG B_gu^T) on the
+// streamed path, for rs <= 64 (prepass.hip).
+enum PrepassKind { PRE_XA = 0, PRE_HA = 1, PRE_QDN = 2, PRE_QGU = 3 };
+hipError_t stream_prepass(const Layer& L, int kind, hipStream_t st);
 hipError_t stream_gate_up(const Layer& L, hipStream_t st);
 hipError_t stream_down(const Layer& L, hipStream_t st);
 hipError_t stream_dx(const Layer& L, hipStream_t st);
