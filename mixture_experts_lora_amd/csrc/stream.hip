@@ -15,8 +15,11 @@
 // pipeline never drains between tiles: the next tile's first panels are in
 // flight while the current tile's epilogue writes its outputs.
 //
-//  - tile 256 x 256, 4 waves of 128 x 128 (v_mfma_f32_32x32x16_bf16, fp32
-//    accumulation, operands swapped so a lane owns 4 consecutive columns);
+//  - tile 256 x 256, 8 waves of 128 x 64, two per SIMD
+//    (v_mfma_f32_32x32x16_bf16, fp32 accumulation, operands swapped so a
+//    lane owns 4 consecutive columns): while one wave of a SIMD waits to
+//    issue a memory instruction (the CU's queues fill with requests that miss
+//    the L2), the other keeps the SIMD's MFMA unit busy;
 //  - row-contiguous panels are stored [256 rows][32 k] with the 16-byte chunk
 //    of row r at position c ^ ((r >> 2) & 3), read with ds_read_b128;
 //  - panels whose contraction index is the row index in memory (W_dn and
@@ -39,10 +42,10 @@ namespace moe {
 namespace {
 
 constexpr int SBM = 256, SBN = 256;             // tile
-constexpr int SWM = 2, SWN = 2;                 // wave grid
-constexpr int SNW = SWM * SWN, SNT = 64 * SNW;  // 4 waves
-constexpr int STM = SBM / SWM, STN = SBN / SWN; // 128 x 128 per wave
-constexpr int SFM = STM / 32, SFN = STN / 32;   // 4 x 4 fragments
+constexpr int SWM = 2, SWN = 4;                 // wave grid
+constexpr int SNW = SWM * SWN, SNT = 64 * SNW;  // 8 waves, two per SIMD
+constexpr int STM = SBM / SWM, STN = SBN / SWN; // 128 x 64 per wave
+constexpr int SFM = STM / 32, SFN = STN / 32;   // 4 x 2 fragments
 constexpr int SK = 32;                          // k per ring stage
 constexpr int SNS = 4, SPD = SNS - 1;           // ring stages, issue distance
 constexpr int PANEL = SBM * SK;                 // bf16 elements of one operand panel
@@ -54,6 +57,7 @@ static_assert(NI * SNW * 1024 == PANEL * 2, "panel split");
 enum StreamKind { SK_GU = 0, SK_DN = 1, SK_DH = 2, SK_DX = 3 };
 
 typedef unsigned v4u __attribute__((ext_vector_type(4)));
+typedef unsigned v2u __attribute__((ext_vector_type(2)));
 
 typedef short v4s __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) v4s lds_v4s;
@@ -253,10 +257,10 @@ __device__ __forceinline__ void s_issue(const SIssue& S, int step, uint32_t sb, 
   }
 }
 
-// MFMAs of one ring stage, k = 32: the wave's 4 x 4 fragments.  All fragment
-// reads of the stage are issued first (64 VGPRs), then the 32 MFMAs, so the
-// second half's reads land under the first half's MFMAs and LDS latency is
-// exposed once per stage.  (Padding rows are multiplied too: branching around
+// MFMAs of one ring stage, k = 32: the wave's 4 x 2 fragments.  All fragment
+// reads of the stage are issued first, then the 16 MFMAs, so the second
+// half's reads land under the first half's MFMAs and LDS latency is exposed
+// once per stage.  (Padding rows are multiplied too: branching around
 // fragments splits the accumulator's live range and the register allocator
 // then copies it through memory.)
 template <bool BMN>
@@ -308,68 +312,39 @@ __device__ __forceinline__ void s_mma(const bf16_t* As, const bf16_t* Bs, f32x16
   __builtin_amdgcn_sched_group_barrier(0x008, (SK / 16) * SFM * SFN, 0);
 }
 
-// Epilogue, through LDS.  The accumulators stay in AGPRs until they are
-// written (ds_write takes AGPR data): a wave stages a pair of neighbouring
-// 32 x 32 fp32 fragments in its private 8 KiB of the ring stage consumed
-// last (rows of 64 floats, 16-byte chunk c of row m at c ^ (m & 15)), then
-// reads back half a row per lane and writes full 128-byte row segments.
-// Fragment (fm, fn) of the wave covers rows wm 128 + fm 32 + 0..31 and tile
-// columns wn 128 + fn 32 + 0..31; lane l holds row l % 32, columns
-// 8 g + 4 (l / 32) + 0..3 in elements 4 g + 0..3.
-__device__ __forceinline__ void s_stage_pair(float* wl, const f32x16& v0, const f32x16& v1) {
+// Epilogue, through a private 4 KiB LDS staging area per wave.  The
+// accumulators of a pair of neighbouring 32 x 32 fragments (fn = 2 pr, 2 pr
+// + 1) are rounded to bf16 and written as rows of 64 values (128 bytes, the
+// 16-byte chunk c of row m at c ^ (m & 7)); they are read back by rows, lane
+// -> row (lane / 8) + 8 i, chunk lane % 8, so that each store instruction
+// writes 8 whole 128-byte row segments.  Fragment (fm, fn) of the wave covers
+// rows wm 128 + fm 32 + 0..31 and tile columns wn 128 + fn 32 + 0..31; lane l
+// holds row l % 32, columns 8 g + 4 (l / 32) + 0..3 in elements 4 g + 0..3.
+__device__ __forceinline__ void s_stage_pair(bf16_t* wl, const f32x16& v0, const f32x16& v1) {
   const int lane = threadIdx.x & 63;
-  const int m = lane & 31;
+  const int m = lane & 31, h = lane >> 5;
 #pragma unroll
-  for (int h = 0; h < 2; ++h) {
-    const f32x16& v = h ? v1 : v0;
+  for (int f = 0; f < 2; ++f) {
+    const f32x16& v = f ? v1 : v0;
 #pragma unroll
     for (int g = 0; g < 4; ++g) {
-      const int c = h * 8 + 2 * g + (lane >> 5);
-      *(float4*)(wl + m * 64 + ((c ^ (m & 15)) * 4)) =
-          make_float4(v[4 * g], v[4 * g + 1], v[4 * g + 2], v[4 * g + 3]);
+      const int c = 4 * f + g;
+      *(uint2*)(wl + m * 64 + ((c ^ (m & 7)) * 8) + 4 * h) =
+          make_uint2(pack2(v[4 * g], v[4 * g + 1]), pack2(v[4 * g + 2], v[4 * g + 3]));
     }
   }
 }
-// Row lane / 2 of the staged pair, columns 32 (lane % 2) .. + 32 of the 64.
-__device__ __forceinline__ void s_unstage(const float* wl, float (&f)[32]) {
+__device__ __forceinline__ uint4 s_unstage(const bf16_t* wl, int i) {
   const int lane = threadIdx.x & 63;
-  const int rr = lane >> 1, hc = (lane & 1) * 8;
-#pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    const float4 q = *(const float4*)(wl + rr * 64 + (((hc + i) ^ (rr & 15)) * 4));
-    f[4 * i] = q.x;
-    f[4 * i + 1] = q.y;
-    f[4 * i + 2] = q.z;
-    f[4 * i + 3] = q.w;
-  }
+  const int r = (lane >> 3) + 8 * i, c = lane & 7;
+  return *(const uint4*)(wl + r * 64 + ((c ^ (r & 7)) * 8));
 }
-// 16 bf16 values at byte voff of the buffer: exactly two store instructions,
-// also for padding rows (voff out of range: the stores are dropped), so
-// every wave issues the same known number of stores per tile.
-// Row lane / 8 + 8 i (i = 0..3) of the staged pair, columns 8 (lane % 8)
-// .. + 8: each store instruction then writes 8 whole 128-byte row segments.
-__device__ __forceinline__ void s_unstage_rows(const float* wl, int i, float (&f)[8]) {
-  const int lane = threadIdx.x & 63;
-  const int r = (lane >> 3) + 8 * i, c = (lane & 7) * 2;
-#pragma unroll
-  for (int h = 0; h < 2; ++h) {
-    const float4 q = *(const float4*)(wl + r * 64 + (((c + h) ^ (r & 15)) * 4));
-    f[4 * h] = q.x;
-    f[4 * h + 1] = q.y;
-    f[4 * h + 2] = q.z;
-    f[4 * h + 3] = q.w;
-  }
-}
-__device__ __forceinline__ void s_store8(rsrc_t r, uint32_t voff, const float* f) {
-  const v4u a = {pack2(f[0], f[1]), pack2(f[2], f[3]), pack2(f[4], f[5]), pack2(f[6], f[7])};
+__device__ __forceinline__ void s_store(rsrc_t r, uint32_t voff, uint4 v) {
+  const v4u a = {v.x, v.y, v.z, v.w};
   __builtin_amdgcn_raw_buffer_store_b128(a, r, voff, 0, 0);
 }
-__device__ __forceinline__ void s_store16(rsrc_t r, uint32_t voff, const float* f) {
-  const v4u a = {pack2(f[0], f[1]), pack2(f[2], f[3]), pack2(f[4], f[5]), pack2(f[6], f[7])};
-  const v4u b = {pack2(f[8], f[9]), pack2(f[10], f[11]), pack2(f[12], f[13]), pack2(f[14], f[15])};
-  __builtin_amdgcn_raw_buffer_store_b128(a, r, voff, 0, 0);
-  __builtin_amdgcn_raw_buffer_store_b128(b, r, voff + 16u, 0, 0);
-}
+__device__ __forceinline__ float s_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float s_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
 
 // dh epilogue: dH (without the routing weight) of fragment pair (fm, pr) is
 // staged as above and read back by rows: lane -> row (lane / 8) + 8 i,
@@ -400,7 +375,7 @@ __device__ __forceinline__ void s_dh_load(const Layer& L, const STile& T, rsrc_t
     o.w[i] = __uint_as_float((uint32_t)__builtin_amdgcn_raw_buffer_load_b32(rw, ok ? (uint32_t)(T.row0 + m) * 4u : OOB, 0, 0));
   }
 }
-__device__ __forceinline__ void s_epilogue_dh(const Layer& L, const STile& T, f32x16 (&acc)[SFM][SFN], float* wl) {
+__device__ __forceinline__ void s_epilogue_dh(const Layer& L, const STile& T, f32x16 (&acc)[SFM][SFN], bf16_t* wl) {
   const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
   const int wm = wid / SWN, wn = wid % SWN;
   const int n = L.n;
@@ -417,8 +392,8 @@ __device__ __forceinline__ void s_epilogue_dh(const Layer& L, const STile& T, f3
     const int j = T.nt * SBN + wn * STN + pr * 64 + (lane & 7) * 8;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      float f8[8];
-      s_unstage_rows(wl, i, f8);
+      const uint4 v = s_unstage(wl, i);
+      const uint32_t dw[4] = {v.x, v.y, v.z, v.w};
       const int m = wm * STM + fm * 32 + (lane >> 3) + 8 * i;
       const bool ok = m < T.mrows && j < n;
       const int64_t p = T.row0 + m;
@@ -426,18 +401,24 @@ __device__ __forceinline__ void s_epilogue_dh(const Layer& L, const STile& T, f3
       const float w = cur.w[i];
       const uint32_t gw[4] = {cur.g[i].x, cur.g[i].y, cur.g[i].z, cur.g[i].w};
       const uint32_t uw[4] = {cur.u[i].x, cur.u[i].y, cur.u[i].z, cur.u[i].w};
-      float dgt[8], dup[8];
+      uint32_t dgt[4], dup[4];
 #pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const float gv = bf2f((bf16_t)((e & 1) ? gw[e >> 1] >> 16 : gw[e >> 1] & 0xffffu));
-        const float uv = bf2f((bf16_t)((e & 1) ? uw[e >> 1] >> 16 : uw[e >> 1] & 0xffffu));
-        const float dh = w * f8[e];
-        const float sg = sigmoid_f(gv);
-        dgt[e] = dh * uv * (sg * (1.0f + gv * (1.0f - sg)));
-        dup[e] = dh * (gv * sg);
+      for (int e2 = 0; e2 < 4; ++e2) {
+        float rg2[2], ru2[2];
+#pragma unroll
+        for (int hh = 0; hh < 2; ++hh) {
+          const float gv = hh ? s_hi(gw[e2]) : s_lo(gw[e2]);
+          const float uv = hh ? s_hi(uw[e2]) : s_lo(uw[e2]);
+          const float dh = w * (hh ? s_hi(dw[e2]) : s_lo(dw[e2]));
+          const float sg = sigmoid_f(gv);
+          rg2[hh] = dh * uv * (sg * (1.0f + gv * (1.0f - sg)));
+          ru2[hh] = dh * (gv * sg);
+        }
+        dgt[e2] = pack2(rg2[0], rg2[1]);
+        dup[e2] = pack2(ru2[0], ru2[1]);
       }
-      s_store8(rdg, og, dgt);
-      s_store8(rdg, ok ? og + (uint32_t)(n * 2) : OOB, dup);
+      s_store(rdg, og, make_uint4(dgt[0], dgt[1], dgt[2], dgt[3]));
+      s_store(rdg, ok ? og + (uint32_t)(n * 2) : OOB, make_uint4(dup[0], dup[1], dup[2], dup[3]));
     }
     if (q + 1 < SFM * (SFN / 2)) cur = nxt;
   }
@@ -446,16 +427,16 @@ __device__ __forceinline__ void s_epilogue_dh(const Layer& L, const STile& T, f3
 // Store instructions each wave issues in one tile's epilogue.
 template <int KIND>
 constexpr int s_epi_stores() {
-  // per fragment pair: GU 3 outputs x 2; DH 4 rows x (dgate, dup); else 4 rows
-  return SFM * (SFN / 2) * (KIND == SK_GU ? 6 : KIND == SK_DH ? 8 : 4);
+  // per fragment pair and readback row group: GU G and H; DH dgate and dup;
+  // else one
+  return SFM * (SFN / 2) * 4 * (KIND == SK_GU || KIND == SK_DH ? 2 : 1);
 }
 
 template <int KIND>
-__device__ __forceinline__ void s_epilogue(const Layer& L, const STile& T, f32x16 (&acc)[SFM][SFN], float* wl) {
+__device__ __forceinline__ void s_epilogue(const Layer& L, const STile& T, f32x16 (&acc)[SFM][SFN], bf16_t* wl) {
   static_assert(KIND != SK_DH, "dh has its own epilogue");
   const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
   const int wm = wid / SWN, wn = wid % SWN;
-  const int rr = lane >> 1, half = lane & 1;
   const int n = L.n, d = L.d;
   const int64_t P = L.Ptot;
   const rsrc_t rg = make_rsrc(L.g, P * 2 * n * 2), rh = make_rsrc(L.h, P * n * 2), ro = make_rsrc(L.o, P * d * 2);
@@ -464,55 +445,43 @@ __device__ __forceinline__ void s_epilogue(const Layer& L, const STile& T, f32x1
 #pragma unroll
     for (int pr = 0; pr < SFN / 2; ++pr) {
       s_stage_pair(wl, acc[fm][2 * pr], acc[fm][2 * pr + 1]);
-      if constexpr (KIND != SK_GU) {
-        const int c = T.nt * SBN + wn * STN + pr * 64 + (lane & 7) * 8;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          float f8[8];
-          s_unstage_rows(wl, i, f8);
-          const int m = wm * STM + fm * 32 + (lane >> 3) + 8 * i;
+      for (int i = 0; i < 4; ++i) {
+        const uint4 v = s_unstage(wl, i);
+        const int m = wm * STM + fm * 32 + (lane >> 3) + 8 * i;
+        const int64_t p = T.row0 + m;
+        if constexpr (KIND == SK_GU) {
+          // chunks 0..3 of the pair are gate(j), 4..7 up(j) for j = jb + 8
+          // (chunk % 4) + 0..7: each lane stores its own chunk of G, and the
+          // two lanes holding gate and up of the same j compute 4 h each
+          const int c = lane & 7, up = c >> 2;
+          const int j = T.nt * (SBN / 2) + (wn * (SFN / 2) + pr) * 32 + 8 * (c & 3);
+          const bool ok = m < T.mrows && j < n;
+          s_store(rg, ok ? (uint32_t)((p * 2 * n + (up ? n : 0) + j) * 2) : OOB, v);
+          const uint32_t o[4] = {(uint32_t)__shfl_xor((int)v.x, 4, 64), (uint32_t)__shfl_xor((int)v.y, 4, 64),
+                                 (uint32_t)__shfl_xor((int)v.z, 4, 64), (uint32_t)__shfl_xor((int)v.w, 4, 64)};
+          const uint32_t mine[4] = {v.x, v.y, v.z, v.w};
+          // lane with the gate chunk takes values 0..3, its partner 4..7
+          uint32_t hw[2];
+#pragma unroll
+          for (int e2 = 0; e2 < 2; ++e2) {
+            const uint32_t gw = up ? o[2 * up + e2] : mine[e2];
+            const uint32_t uw = up ? mine[2 * up + e2] : o[e2];
+            hw[e2] = pack2(silu_f(s_lo(gw)) * s_lo(uw), silu_f(s_hi(gw)) * s_hi(uw));
+          }
+          const uint32_t oh = ok ? (uint32_t)((p * n + j + 4 * up) * 2) : OOB;
+          __builtin_amdgcn_raw_buffer_store_b64((v2u){hw[0], hw[1]}, rh, oh, 0, 0);
+        } else {
+          const int c = T.nt * SBN + wn * STN + pr * 64 + (lane & 7) * 8;
           const bool ok = m < T.mrows && c < d;
-          s_store8(ro, ok ? (uint32_t)(((int64_t)(T.row0 + m) * d + c) * 2) : OOB, f8);
+          s_store(ro, ok ? (uint32_t)((p * d + c) * 2) : OOB, v);
         }
-        continue;
-      }
-      float f[32];
-      s_unstage(wl, f);
-      const int m = wm * STM + fm * 32 + rr;
-      const int64_t p = T.row0 + m;
-      if constexpr (KIND == SK_GU) {
-        // columns 0..31 of the pair are gate(j), 32..63 up(j), j = jb + 0..31;
-        // the two lanes of a row split j = jb + 16 half + 0..15
-        const int j = T.nt * (SBN / 2) + (wn * (SFN / 2) + pr) * 32 + 16 * half;
-        const bool ok = m < T.mrows && j < n;
-        float gv[16], uv[16], hv[16];
-#pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          const float lo = f[i], hi = f[16 + i];  // static indices: no select chains
-          const float mine = half ? hi : lo;
-          const float other = __shfl_xor(half ? lo : hi, 1, 64);
-          gv[i] = half ? other : mine;
-          uv[i] = half ? mine : other;
-          hv[i] = silu_f(gv[i]) * uv[i];
-        }
-        const uint32_t og = ok ? (uint32_t)((p * 2 * n + j) * 2) : OOB;
-        const uint32_t ou = ok ? (uint32_t)((p * 2 * n + n + j) * 2) : OOB;
-        const uint32_t oh = ok ? (uint32_t)((p * n + j) * 2) : OOB;
-        s_store16(rg, og, gv);
-        s_store16(rg, ou, uv);
-        s_store16(rh, oh, hv);
-      } else {
-        const int c = T.nt * SBN + wn * STN + pr * 64 + 32 * half;
-        const bool ok = m < T.mrows && c < d;
-        const uint32_t oo = ok ? (uint32_t)((p * d + c) * 2) : OOB;
-        s_store16(ro, oo, f);
-        s_store16(ro, ok ? oo + 32u : OOB, f + 16);
       }
     }
 }
 
 template <int KIND>
-__global__ __launch_bounds__(SNT) __attribute__((amdgpu_waves_per_eu(1, 1))) void k_stream(const Layer L) {
+__global__ __launch_bounds__(SNT) __attribute__((amdgpu_waves_per_eu(SNW / 4, SNW / 4))) void k_stream(const Layer L) {
   __shared__ __attribute__((aligned(1024))) bf16_t ring[SNS * SSTAGE];
   __shared__ __attribute__((aligned(16))) int tokbuf[2][SBM];
   __shared__ int pre[MAX_ET + 1];
@@ -620,9 +589,9 @@ __global__ __launch_bounds__(SNT) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
     // every wave is done reading it
     __syncthreads();
     if constexpr (KIND == SK_DH)
-      s_epilogue_dh(L, tcur, acc, (float*)(ring + ((gc + SNS - 1) % SNS) * SSTAGE) + wid * 2048);
+      s_epilogue_dh(L, tcur, acc, ring + ((gc + SNS - 1) % SNS) * SSTAGE + wid * 2048);
     else
-      s_epilogue<KIND>(L, tcur, acc, (float*)(ring + ((gc + SNS - 1) % SNS) * SSTAGE) + wid * 2048);
+      s_epilogue<KIND>(L, tcur, acc, ring + ((gc + SNS - 1) % SNS) * SSTAGE + wid * 2048);
     after_epi = true;
   }
   wait_vmcnt<0>();
