@@ -45,8 +45,11 @@ tests):
     do not say how alpha is applied);
   * one shared expert, when present, is stacked as expert E with weight 1 for
     every token and is not routed;
-  * the router is frozen: no gradient for logits or routing weights, none for
-    the frozen base weights.
+  * the router is frozen in the layer's backward: it produces no gradient for
+    logits or routing weights, none for the frozen base weights;
+    ``router_grads`` gives the routing-weight and logit gradients separately,
+    for a model whose router is trained (the selection is taken as locally
+    constant, the shared expert's weight as the constant 1).
 
 Arithmetic: float64 by default (float32 on request, used for timing); bf16
 inputs are decoded exactly; no intermediate rounding.
@@ -72,6 +75,7 @@ __all__ = [
     "backward",
     "backward_tokens",
     "lora_grads_expert",
+    "router_grads",
 ]
 
 
@@ -410,3 +414,30 @@ def lora_grads_expert(inp, topk_ids, topk_w, dims, e, dtype=np.float64):
         return (np.zeros((dims.d, dims.r), dtype), np.zeros((dims.r, 2 * n), dtype),
                 np.zeros((n, dims.r), dtype), np.zeros((dims.r, dims.d), dtype))
     return _expert_backward(X[tok], wt * dY[tok], W, e, n, s)[1:]
+
+
+# ----------------------------------------------------------------------------
+# Gradients that reach the router (beyond the pages' frozen router)
+# ----------------------------------------------------------------------------
+
+def router_grads(inp, topk_ids, topk_w, dims, dtype=np.float64):
+    """Routing-weight and logit gradients of the layer, given dY (``inp.dy``).
+
+    Y[t] is linear in the routing weights, so
+      d_topk_w[t, j] = <dY[t], O(t, expert j)>;
+    w[t, :] is the softmax of the k selected logits, whose Jacobian is
+    dw_j / dl_i = w_j (delta_ij - w_i), so
+      d_logits[t, ids[t, i]] = w[t, i] (d_topk_w[t, i] - sum_j w[t, j] d_topk_w[t, j]),
+    and the logits of experts not selected get 0 (a small change leaves the
+    selection as it is).  The shared expert's weight is the constant 1.
+    """
+    T, k, E = dims.T, dims.k, dims.E
+    fw = forward(inp, topk_ids, topk_w, dims, dtype)
+    dY = bf16_decode(inp.dy, dtype)
+    o = fw["o_pair"][:T * k].reshape(T, k, dims.d)
+    dw = (dY[:, None, :] * o).sum(axis=2)
+    w = np.asarray(topk_w, dtype=np.float32).astype(dtype)
+    dsel = w * (dw - (w * dw).sum(axis=1, keepdims=True))
+    dl = np.zeros((T, E), dtype)
+    dl[np.arange(T)[:, None], np.asarray(topk_ids, dtype=np.int64)] = dsel
+    return {"d_topk_w": dw, "d_logits": dl}
