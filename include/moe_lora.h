@@ -148,19 +148,31 @@ moe_status moe_lora_forward(const moe_dims* dims, const moe_bf16* x, const moe_r
                             const moe_weights* weights, moe_bf16* y, void* saved,
                             size_t saved_bytes, void* ws, size_t ws_bytes, void* stream);
 
-/* Backward for dX and the LoRA factors (the router and base weights are
- * frozen, so no gradient is produced for them):
+/* Backward for dX and the LoRA factors (the pages freeze the router and the
+ * base weights; no gradient is produced for the base weights):
  *   dy   bf16 [T, d] upstream gradient;  x as given to forward
  *   saved  the buffer forward filled, with the same dims/routing/weights
  *   dx   bf16 [T, d]
  *   da_gate_up fp32 [E_tot, d, r]   db_gate_up fp32 [E_tot, r, 2n]
  *   da_down    fp32 [E_tot, n, r]   db_down    fp32 [E_tot, r, d]
+ *   d_topk_w   fp32 [T, k] or NULL: gradient w.r.t. the routing weights,
+ *              d w[t,j] = <dY[t], O(t,j)> (Y is linear in w; O is the pair's
+ *              down output before the weight)
+ *   d_logits   fp32 [T, E] or NULL: gradient w.r.t. the router logits through
+ *              the softmax over the k selected logits,
+ *              d logit[t, id_j] = w_j (d w_j - sum_i w_i d w_i), 0 for the
+ *              experts not selected (the selection is locally constant); the
+ *              shared expert's weight is the constant 1 and takes none.
+ *              For models that train the router (the pages freeze it).
+ *              MOE_ERROR_UNSUPPORTED if this build's dh kernel cannot supply
+ *              the dot products.
  *   ws   scratch of moe_workspace_bytes(dims) */
 moe_status moe_lora_backward(const moe_dims* dims, const moe_bf16* dy, const moe_bf16* x,
                              const moe_routing* routing, const moe_weights* weights,
                              const void* saved, size_t saved_bytes, moe_bf16* dx,
                              float* da_gate_up, float* db_gate_up, float* da_down,
-                             float* db_down, void* ws, size_t ws_bytes, void* stream);
+                             float* db_down, float* d_topk_w, float* d_logits, void* ws,
+                             size_t ws_bytes, void* stream);
 
 /* Kernel timing, for measurement tools (not part of the layer's math).
  * moe_timing_enable(1) starts recording: every kernel the library enqueues

@@ -9,10 +9,12 @@ from .api import (  # noqa: F401
     Dims,
     Grads,
     MoELoRALayer,
+    RouterGrads,
     Routing,
     Weights,
     backward,
     empty_grads,
+    empty_router_grads,
     empty_routing,
     forward,
     forward_saved_bytes,

@@ -74,7 +74,7 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.moe_lora_forward.restype = ctypes.c_int
     lib.moe_lora_forward.argtypes = [pd, vp, pr, pw, vp, vp, sz, vp, sz, vp]
     lib.moe_lora_backward.restype = ctypes.c_int
-    lib.moe_lora_backward.argtypes = [pd, vp, vp, pr, pw, vp, sz, vp, vp, vp, vp, vp, vp, sz, vp]
+    lib.moe_lora_backward.argtypes = [pd, vp, vp, pr, pw, vp, sz, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
     lib.moe_timing_enable.restype = ctypes.c_int
     lib.moe_timing_enable.argtypes = [ctypes.c_int]
     lib.moe_timing_report.restype = ctypes.c_int

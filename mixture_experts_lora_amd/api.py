@@ -68,6 +68,12 @@ class Grads(NamedTuple):
     db_down: torch.Tensor     # fp32 [E_tot, r, d]
 
 
+class RouterGrads(NamedTuple):
+    """Gradients that reach the router, for models that train it."""
+    d_topk_w: torch.Tensor    # fp32 [T, k]
+    d_logits: torch.Tensor    # fp32 [T, E]
+
+
 def _ptr(t: Optional[torch.Tensor]) -> Optional[int]:
     return None if t is None else t.data_ptr()
 
@@ -193,10 +199,17 @@ def empty_grads(dims: Dims, device) -> Grads:
                  torch.empty(Et, r, d, dtype=f32, device=device))
 
 
+def empty_router_grads(dims: Dims, device) -> RouterGrads:
+    return RouterGrads(torch.empty(dims.T, dims.k, dtype=torch.float32, device=device),
+                       torch.empty(dims.T, dims.E, dtype=torch.float32, device=device))
+
+
 def backward(dy: torch.Tensor, x: torch.Tensor, routing: Routing, weights: Weights,
              saved: torch.Tensor, dims: Dims, out: Optional[Grads] = None,
-             ws: Optional[torch.Tensor] = None, stream=None) -> Grads:
-    """moe_lora_backward: dX and the LoRA-factor gradients."""
+             ws: Optional[torch.Tensor] = None, stream=None,
+             router_out: Optional[RouterGrads] = None) -> Grads:
+    """moe_lora_backward: dX and the LoRA-factor gradients; with ``router_out``
+    also the routing-weight and logit gradients (written into it)."""
     lib = _lib.load()
     _check(dy, (dims.T, dims.d), torch.bfloat16, "dy")
     _check(x, (dims.T, dims.d), torch.bfloat16, "x")
@@ -209,6 +222,11 @@ def backward(dy: torch.Tensor, x: torch.Tensor, routing: Routing, weights: Weigh
     _check(out.db_gate_up, (Et, r, 2 * n), torch.float32, "db_gate_up")
     _check(out.da_down, (Et, n, r), torch.float32, "da_down")
     _check(out.db_down, (Et, r, d), torch.float32, "db_down")
+    dtw = dlg = None
+    if router_out is not None:
+        _check(router_out.d_topk_w, (dims.T, dims.k), torch.float32, "d_topk_w")
+        _check(router_out.d_logits, (dims.T, dims.E), torch.float32, "d_logits")
+        dtw, dlg = router_out.d_topk_w.data_ptr(), router_out.d_logits.data_ptr()
     if ws is None:
         ws = _bytes(workspace_bytes(dims), dy.device)
     dc, rc, wc = dims.c(), _c_routing(routing), _c_weights(weights)
@@ -216,7 +234,7 @@ def backward(dy: torch.Tensor, x: torch.Tensor, routing: Routing, weights: Weigh
                                      ctypes.byref(rc), ctypes.byref(wc), saved.data_ptr(),
                                      saved.numel(), out.dx.data_ptr(), out.da_gate_up.data_ptr(),
                                      out.db_gate_up.data_ptr(), out.da_down.data_ptr(),
-                                     out.db_down.data_ptr(), ws.data_ptr(), ws.numel(),
+                                     out.db_down.data_ptr(), dtw, dlg, ws.data_ptr(), ws.numel(),
                                      _stream(stream)),
                "moe_lora_backward")
     return out
@@ -235,6 +253,7 @@ class MoELoRALayer:
         self.ws = _bytes(workspace_bytes(dims), device)
         self.y = torch.empty(dims.T, dims.d, dtype=torch.bfloat16, device=device)
         self.grads = empty_grads(dims, device)
+        self.router_grads: Optional[RouterGrads] = None
 
     def route(self, logits, stream=None) -> Routing:
         return route(logits, self.dims, self.routing, self.route_ws, stream)
@@ -243,6 +262,9 @@ class MoELoRALayer:
         forward(x, self.routing, self.weights, self.dims, self.y, self.saved, self.ws, stream)
         return self.y
 
-    def backward(self, dy, x, stream=None) -> Grads:
+    def backward(self, dy, x, stream=None, router: bool = False) -> Grads:
+        """dX and the LoRA gradients; with ``router`` also ``self.router_grads``."""
+        if router and self.router_grads is None:
+            self.router_grads = empty_router_grads(self.dims, self.y.device)
         return backward(dy, x, self.routing, self.weights, self.saved, self.dims, self.grads,
-                        self.ws, stream)
+                        self.ws, stream, self.router_grads if router else None)

@@ -90,6 +90,8 @@ void attach_common(Layer& L, const moe_routing* rt, const moe_weights* w, const 
   L.qgu = (bf16_t*)(base + wl.qgu);
   L.hw = (bf16_t*)(base + wl.hw);
   L.qw = (bf16_t*)(base + wl.qw);
+  L.dw_part = nullptr;  // set by backward when router gradients are requested
+  L.dw_groups = dm->n / 64;
   L.partial = (float*)(base + wl.partial);
   L.pre_partial = (float*)(base + wl.pre_partial);
   for (int i = 0; i < 4; ++i) L.partial_off[i] = wl.partial_off[i];
@@ -183,8 +185,9 @@ moe_status moe_lora_forward(const moe_dims* dm, const moe_bf16* x, const moe_rou
 moe_status moe_lora_backward(const moe_dims* dm, const moe_bf16* dy, const moe_bf16* x,
                              const moe_routing* rt, const moe_weights* w, const void* saved,
                              size_t saved_bytes, moe_bf16* dx, float* da_gate_up,
-                             float* db_gate_up, float* da_down, float* db_down, void* ws,
-                             size_t ws_bytes, void* stream) {
+                             float* db_gate_up, float* da_down, float* db_down,
+                             float* d_topk_w, float* d_logits, void* ws, size_t ws_bytes,
+                             void* stream) {
   moe_status st = check_dims(dm);
   if (st != MOE_SUCCESS) return st;
   if ((st = check_routing_in(rt)) != MOE_SUCCESS) return st;
@@ -193,6 +196,10 @@ moe_status moe_lora_backward(const moe_dims* dm, const moe_bf16* dy, const moe_b
       !aligned16(da_gate_up) || !aligned16(db_gate_up) || !aligned16(da_down) ||
       !aligned16(db_down) || !aligned16(ws))
     return MOE_ERROR_INVALID_VALUE;
+  if ((d_topk_w && !aligned16(d_topk_w)) || (d_logits && !aligned16(d_logits)))
+    return MOE_ERROR_INVALID_VALUE;
+  const bool router = d_topk_w || d_logits;
+  if (router && !dh_writes_router_partials()) return MOE_ERROR_UNSUPPORTED;
   if (saved_bytes < moe_forward_saved_bytes(dm) || ws_bytes < moe_workspace_bytes(dm))
     return MOE_ERROR_WORKSPACE;
   hipStream_t s = (hipStream_t)stream;
@@ -206,8 +213,12 @@ moe_status moe_lora_backward(const moe_dims* dm, const moe_bf16* dy, const moe_b
   L.db_gu = db_gate_up;
   L.da_dn = da_down;
   L.db_dn = db_down;
+  if (router)
+    L.dw_part = (float*)((char*)ws + ws_layout(dm->T, dm->d, dm->n, dm->E, dm->k, dm->r,
+                                               dm->n_shared).dw_part);
   hipError_t e = maybe_pack(L, w, s);
   if (e == hipSuccess) e = gemm_dh(L, s);
+  if (e == hipSuccess && router) e = launch_router_grad(L, d_topk_w, d_logits, s);
   if (e == hipSuccess) e = gemm_dx(L, s);
   if (e == hipSuccess) e = launch_combine(L, false, L.o, L.dx, s);
   if (e == hipSuccess) e = gemm_lora_grads(L, s);

@@ -1162,6 +1162,8 @@ hipError_t gemm_dh(const Layer& L, hipStream_t st) {
   return hipGetLastError();
 }
 
+bool dh_writes_router_partials() { return MOE_STREAM_DH != 0; }
+
 hipError_t gemm_dx(const Layer& L, hipStream_t st) {
   using C = MainCfg<MOE_CFG_DX>::type;
   launch_prepass<PRE_QGU>(L, st, "prepass_qgu");

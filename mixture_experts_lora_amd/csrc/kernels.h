@@ -46,6 +46,8 @@ struct Layer {
   bf16_t* qgu;       // [Ptot, rs]
   bf16_t* hw;        // [Ptot, rs]  w * s H A_dn (dB_dn operand)
   bf16_t* qw;        // [Ptot, rs]  w * Q_dn (dA_dn operand)
+  float* dw_part;    // [Ptot, n / 64] partial <dH, H> per 64-column group, or null
+  int dw_groups;     // n / 64
   bf16_t* y;         // [T, d]
   bf16_t* dx;        // [T, d]
   float* da_gu;      // [Et, d, r]
@@ -68,7 +70,7 @@ __host__ __device__ inline void grad_shape(int kind, int d, int n, int r, int& M
 
 // Workspace carving shared by the size query and the launchers.
 struct WsLayout {
-  size_t o, dg, qdn, qgu, hw, qw, partial, pre_partial, a_gu_pack, a_dn_pack, total;
+  size_t o, dg, qdn, qgu, hw, qw, dw_part, partial, pre_partial, a_gu_pack, a_dn_pack, total;
   int64_t partial_off[4];
 };
 struct SavedLayout {
@@ -104,6 +106,10 @@ hipError_t dma_lora_grads(const Layer& L, hipStream_t st);
 hipError_t launch_pack_a(const Layer& L, const bf16_t* a_gu_src, const bf16_t* a_dn_src,
                          bf16_t* a_gu_dst, bf16_t* a_dn_dst, hipStream_t st);
 hipError_t launch_gather_table(const Layer& L, int32_t* tok, float* wgt, hipStream_t st);
+// Routing-weight and logit gradients from the dh epilogue's partials.
+hipError_t launch_router_grad(const Layer& L, float* d_topk_w, float* d_logits, hipStream_t st);
+// Whether gemm_dh writes the <dH, H> partials (the streamed dh does).
+bool dh_writes_router_partials();
 hipError_t launch_combine(const Layer& L, bool weighted, const bf16_t* src, bf16_t* dst,
                           hipStream_t st);
 

@@ -22,6 +22,7 @@ WsLayout ws_layout(int64_t T, int d, int n, int E, int k, int r, int S) {
   w.qgu = off;      off += align256((size_t)Ptot * rs * 2);
   w.hw = off;       off += align256((size_t)Ptot * rs * 2);
   w.qw = off;       off += align256((size_t)Ptot * rs * 2);
+  w.dw_part = off;  off += align256((size_t)Ptot * (n / 64) * 4);
   const int64_t slots = Ptot / SPLITK_ROWS + Et;
   int64_t pf = 0;
   for (int kind = 0; kind < 4; ++kind) {
@@ -153,6 +154,48 @@ __global__ __launch_bounds__(256) void k_combine(const Layer L, int weighted,
         make_uint4(pack2(acc[0], acc[1]), pack2(acc[2], acc[3]), pack2(acc[4], acc[5]),
                    pack2(acc[6], acc[7]));
   }
+}
+
+// Gradients that reach the router (for a model that trains it; the layer's
+// own backward leaves the router frozen, "Faster LoRA MoE training").  Y[t]
+// is linear in the routing weights, so d w[t, j] = <dY[t], O(t, j)>, which
+// equals <dH, H> over the pair's row with dH taken before the routing weight
+// (the dh epilogue leaves those dot products per 64-column group in
+// dw_part).  Through the softmax over the k selected logits:
+// d logit[t, id_j] = w_j (dw_j - sum_i w_i dw_i); the other logits get 0.
+// One wave per token; sums run in a fixed order.
+__global__ __launch_bounds__(64) void k_router_grad(const Layer L, float* __restrict__ d_topk_w,
+                                                    float* __restrict__ d_logits) {
+  __shared__ float row[256];  // E <= 256 (validated at the boundary), k <= E
+  __shared__ float dwv[256];
+  const int t = blockIdx.x, lane = threadIdx.x;
+  const int k = L.k, E = L.E, G = L.dw_groups;
+  float part = 0.0f;
+  for (int j = lane; j < k; j += 64) {
+    const int64_t p = L.pair_pos[(int64_t)t * k + j];
+    const float* src = L.dw_part + p * G;
+    float sdw = 0.0f;
+    for (int g = 0; g < G; ++g) sdw += src[g];
+    dwv[j] = sdw;
+    if (d_topk_w) d_topk_w[(int64_t)t * k + j] = sdw;
+    part += L.topk_w[(int64_t)t * k + j] * sdw;
+  }
+  if (!d_logits) return;
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) part += __shfl_xor(part, off, 64);
+  for (int e = lane; e < E; e += 64) row[e] = 0.0f;
+  __syncthreads();
+  for (int j = lane; j < k; j += 64) {
+    const float w = L.topk_w[(int64_t)t * k + j];
+    row[L.topk_ids[(int64_t)t * k + j]] = w * (dwv[j] - part);
+  }
+  __syncthreads();
+  for (int e = lane; e < E; e += 64) d_logits[(int64_t)t * E + e] = row[e];
+}
+
+hipError_t launch_router_grad(const Layer& L, float* d_topk_w, float* d_logits, hipStream_t st) {
+  MOE_LAUNCH("router_grad", k_router_grad, dim3(L.T), dim3(64), 0, st, L, d_topk_w, d_logits);
+  return hipGetLastError();
 }
 
 hipError_t launch_combine(const Layer& L, bool weighted, const bf16_t* src, bf16_t* dst,

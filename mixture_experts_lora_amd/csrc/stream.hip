@@ -382,6 +382,10 @@ __device__ __forceinline__ void s_epilogue_dh(const Layer& L, const STile& T, f3
   const int64_t P = L.Ptot;
   const rsrc_t rg = make_rsrc(L.g, P * 2 * n * 2), rdg = make_rsrc(L.dg, P * 2 * n * 2);
   const rsrc_t rw = make_rsrc(L.wgt, P * 4);
+  // <dH, H> of each row over each 64-column group, for the routing-weight
+  // gradient; without a destination every such store falls out of range
+  const int G = L.dw_groups;
+  const rsrc_t rpart = make_rsrc(L.dw_part, L.dw_part ? P * G * 4 : 0);
   GUq cur, nxt;
   s_dh_load(L, T, rg, rw, 0, cur);
 #pragma unroll
@@ -402,6 +406,7 @@ __device__ __forceinline__ void s_epilogue_dh(const Layer& L, const STile& T, f3
       const uint32_t gw[4] = {cur.g[i].x, cur.g[i].y, cur.g[i].z, cur.g[i].w};
       const uint32_t uw[4] = {cur.u[i].x, cur.u[i].y, cur.u[i].z, cur.u[i].w};
       uint32_t dgt[4], dup[4];
+      float hdot = 0.0f;  // this lane's 8 columns of <dH, H>, dH before w
 #pragma unroll
       for (int e2 = 0; e2 < 4; ++e2) {
         float rg2[2], ru2[2];
@@ -409,16 +414,24 @@ __device__ __forceinline__ void s_epilogue_dh(const Layer& L, const STile& T, f3
         for (int hh = 0; hh < 2; ++hh) {
           const float gv = hh ? s_hi(gw[e2]) : s_lo(gw[e2]);
           const float uv = hh ? s_hi(uw[e2]) : s_lo(uw[e2]);
-          const float dh = w * (hh ? s_hi(dw[e2]) : s_lo(dw[e2]));
+          const float dhu = hh ? s_hi(dw[e2]) : s_lo(dw[e2]);
+          const float dh = w * dhu;
           const float sg = sigmoid_f(gv);
           rg2[hh] = dh * uv * (sg * (1.0f + gv * (1.0f - sg)));
           ru2[hh] = dh * (gv * sg);
+          hdot += dhu * (gv * sg * uv);
         }
         dgt[e2] = pack2(rg2[0], rg2[1]);
         dup[e2] = pack2(ru2[0], ru2[1]);
       }
       s_store(rdg, og, make_uint4(dgt[0], dgt[1], dgt[2], dgt[3]));
       s_store(rdg, ok ? og + (uint32_t)(n * 2) : OOB, make_uint4(dup[0], dup[1], dup[2], dup[3]));
+      // the 8 lanes of a row hold its 64 columns of this pair
+      hdot += __shfl_xor(hdot, 1, 64);
+      hdot += __shfl_xor(hdot, 2, 64);
+      hdot += __shfl_xor(hdot, 4, 64);
+      const uint32_t od = ok && (lane & 7) == 0 ? (uint32_t)((p * G + (j >> 6)) * 4) : OOB;
+      __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(hdot), rpart, od, 0, 0);
     }
     if (q + 1 < SFM * (SFN / 2)) cur = nxt;
   }
@@ -427,9 +440,9 @@ __device__ __forceinline__ void s_epilogue_dh(const Layer& L, const STile& T, f3
 // Store instructions each wave issues in one tile's epilogue.
 template <int KIND>
 constexpr int s_epi_stores() {
-  // per fragment pair and readback row group: GU G and H; DH dgate and dup;
-  // else one
-  return SFM * (SFN / 2) * 4 * (KIND == SK_GU || KIND == SK_DH ? 2 : 1);
+  // per fragment pair and readback row group: GU G and H; DH dgate, dup and
+  // the <dH, H> partial; else one
+  return SFM * (SFN / 2) * 4 * (KIND == SK_GU ? 2 : KIND == SK_DH ? 3 : 1);
 }
 
 template <int KIND>

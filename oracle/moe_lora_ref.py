@@ -76,6 +76,7 @@ __all__ = [
     "backward_tokens",
     "lora_grads_expert",
     "router_grads",
+    "router_grads_tokens",
 ]
 
 
@@ -431,13 +432,34 @@ def router_grads(inp, topk_ids, topk_w, dims, dtype=np.float64):
     and the logits of experts not selected get 0 (a small change leaves the
     selection as it is).  The shared expert's weight is the constant 1.
     """
-    T, k, E = dims.T, dims.k, dims.E
+    T, k = dims.T, dims.k
     fw = forward(inp, topk_ids, topk_w, dims, dtype)
     dY = bf16_decode(inp.dy, dtype)
     o = fw["o_pair"][:T * k].reshape(T, k, dims.d)
     dw = (dY[:, None, :] * o).sum(axis=2)
+    return _softmax_topk_backward(dw, topk_ids, topk_w, dims.E, dtype)
+
+
+def _softmax_topk_backward(dw, topk_ids, topk_w, E, dtype):
     w = np.asarray(topk_w, dtype=np.float32).astype(dtype)
     dsel = w * (dw - (w * dw).sum(axis=1, keepdims=True))
-    dl = np.zeros((T, E), dtype)
-    dl[np.arange(T)[:, None], np.asarray(topk_ids, dtype=np.int64)] = dsel
+    dl = np.zeros((dw.shape[0], E), dtype)
+    dl[np.arange(dw.shape[0])[:, None], np.asarray(topk_ids, dtype=np.int64)] = dsel
     return {"d_topk_w": dw, "d_logits": dl}
+
+
+def router_grads_tokens(inp, topk_ids, topk_w, dims, tokens, dtype=np.float64):
+    """``router_grads`` rows for the listed tokens only (each from its own k
+    pairs, as ``forward_tokens``)."""
+    n, k, s = dims.n, dims.k, dims.lora_scale
+    W = _params(inp, dtype)
+    X = bf16_decode(inp.x, dtype)
+    dY = bf16_decode(inp.dy, dtype)
+    ids = np.asarray(topk_ids)
+    dw = np.zeros((len(tokens), k), dtype)
+    for i, t in enumerate(tokens):
+        for j in range(k):
+            o = expert_forward(X[t:t + 1], W, int(ids[t, j]), n, s)[2][0]
+            dw[i, j] = np.sum(dY[t] * o)
+    tk = np.asarray(tokens)
+    return _softmax_topk_backward(dw, ids[tk], np.asarray(topk_w)[tk], dims.E, dtype)

@@ -105,9 +105,15 @@ def test_null_misaligned_and_small_buffers_rejected(lib):
     assert lib.moe_lora_forward(ctypes.byref(dm), fake, ctypes.byref(rt), ctypes.byref(w), fake,
                                 fake, saved, fake, ws - 1, None) == 3
     assert lib.moe_lora_backward(ctypes.byref(dm), fake, fake, ctypes.byref(rt), ctypes.byref(w),
-                                 fake, saved, fake, fake, fake, fake, fake, fake, ws - 1, None) == 3
+                                 fake, saved, fake, fake, fake, fake, fake, None, None, fake, ws - 1,
+                                 None) == 3
     assert lib.moe_lora_backward(ctypes.byref(dm), fake, fake, ctypes.byref(rt), ctypes.byref(w),
-                                 fake, saved, fake, fake, 0, fake, fake, fake, ws, None) == 1
+                                 fake, saved, fake, fake, 0, fake, fake, None, None, fake, ws,
+                                 None) == 1
+    # the optional router-gradient outputs must be aligned when given
+    assert lib.moe_lora_backward(ctypes.byref(dm), fake, fake, ctypes.byref(rt), ctypes.byref(w),
+                                 fake, saved, fake, fake, fake, fake, fake, fake + 4, None, fake, ws,
+                                 None) == 1
 
 
 def test_python_binding_refuses_cpu_tensors():

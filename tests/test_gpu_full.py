@@ -1,8 +1,9 @@
 """Full-size workloads on the GPU, in the launch configuration bench.py times,
-checked against the oracle on outputs it can compute one by one: Y and dX
-rows of sampled tokens (float64), and the LoRA gradients of sampled experts
-(float32: the least-loaded expert with rows, an empty expert when there is
-one, the most-loaded expert, and the shared expert when there is one).
+checked against the oracle on outputs it can compute one by one: Y, dX and
+router-gradient rows of sampled tokens (float64), and the LoRA gradients of
+sampled experts (float32: the least-loaded expert with rows, an empty expert
+when there is one, the most-loaded expert, and the shared expert when there
+is one).
 Routing at these sizes is compared in full by test_gpu_route."""
 import numpy as np
 import pytest
@@ -31,7 +32,7 @@ def test_full_size_sampled(name):
         t.fill_(float("nan"))
     layer.route(logits)
     y = layer.forward(x)
-    g = layer.backward(dy, x)
+    g = layer.backward(dy, x, router=True)
     torch.cuda.synchronize()
     ids = layer.routing.topk_ids.cpu().numpy()
     tw = layer.routing.topk_w.cpu().numpy()
@@ -42,8 +43,12 @@ def test_full_size_sampled(name):
     dx_ref = oracle.backward_tokens(inp, ids, tw, ld, toks)
     ey = relerr(to_numpy_f64(y)[toks], y_ref)
     edx = relerr(to_numpy_f64(g.dx)[toks], dx_ref)
-    print(f"Y rows {ey:.2e}  dX rows {edx:.2e}", flush=True)
-    assert ey <= TOL and edx <= TOL
+    r_ref = oracle.router_grads_tokens(inp, ids, tw, ld, toks)
+    edw = relerr(to_numpy_f64(layer.router_grads.d_topk_w)[toks], r_ref["d_topk_w"])
+    edl = relerr(to_numpy_f64(layer.router_grads.d_logits)[toks], r_ref["d_logits"])
+    print(f"Y rows {ey:.2e}  dX rows {edx:.2e}  d_topk_w rows {edw:.2e}  d_logits rows {edl:.2e}",
+          flush=True)
+    assert ey <= TOL and edx <= TOL and edw <= TOL and edl <= TOL
     counts = np.bincount(ids.reshape(-1), minlength=ld.E)
     experts = {int(np.argmin(np.where(counts > 0, counts, 1 << 30))), int(np.argmax(counts))}
     if np.any(counts == 0):

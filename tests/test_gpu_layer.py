@@ -1,7 +1,8 @@
 """Forward and backward on the GPU against the float64 oracle, element by
 element, at sizes the oracle finishes in seconds: several M/N tiles, ragged
 segment tails, ranks that are and are not multiples of 8, a shared expert, a
-LoRA scale other than 1, empty experts, split-K LoRA gradients, k = E, T = 1.
+LoRA scale other than 1, empty experts, split-K LoRA gradients, k = E, k = 1,
+T = 1; the routing-weight and logit gradients with every case.
 
 Every output buffer is filled with NaN before the call (an unwritten element
 fails), and the whole route + forward + backward runs twice with bitwise equal
@@ -24,6 +25,7 @@ CASES = {
     "empty_experts_r64": LayerDims(300, 128, 64, 28, 6, 64, logits_recipe="stress"),
     "splitk_two_chunks": LayerDims(2500, 128, 64, 2, 2, 16),
     "k_equals_E": LayerDims(64, 64, 64, 4, 4, 8),
+    "k_one": LayerDims(96, 64, 64, 4, 1, 8),
     "one_token": LayerDims(1, 64, 64, 4, 2, 4),
     "wide_d320_zipf": LayerDims(700, 320, 192, 8, 3, 24, logits_recipe="zipf"),
     # contraction long enough for the rank-r pre-passes to split over workgroups
@@ -36,11 +38,12 @@ def _run(dims, logits, x, dy, w):
     y = torch.full((dims.T, dims.d), float("nan"), dtype=torch.bfloat16, device="cuda")
     y, saved = mel.forward(x, rt, w, dims, y=y)
     g = mel.empty_grads(dims, "cuda")
-    for t in g:
+    rg = mel.empty_router_grads(dims, "cuda")
+    for t in list(g) + list(rg):
         t.fill_(float("nan"))
-    g = mel.backward(dy, x, rt, w, saved, dims, out=g)
+    g = mel.backward(dy, x, rt, w, saved, dims, out=g, router_out=rg)
     torch.cuda.synchronize()
-    return rt, y, g
+    return rt, y, g, rg
 
 
 @pytest.mark.parametrize("name", list(CASES))
@@ -51,17 +54,20 @@ def test_layer_parity(name):
     inp = make_inputs(ld, seed=1)
     dims = mdims(ld)
     logits, x, dy, w = upload(inp)
-    rt, y, g = _run(dims, logits, x, dy, w)
+    rt, y, g, rg = _run(dims, logits, x, dy, w)
     ids = rt.topk_ids.cpu().numpy()
     tw = rt.topk_w.cpu().numpy()
     ref_ids, _ = oracle.topk_softmax(inp.logits, ld.k)
     np.testing.assert_array_equal(ids, ref_ids)
     fw = oracle.forward(inp, ids, tw, ld)
     bw = oracle.backward(inp, ids, tw, ld)
+    rgr = oracle.router_grads(inp, ids, tw, ld)
     got = {"y": y, "dx": g.dx, "da_gu": g.da_gate_up, "db_gu": g.db_gate_up,
-           "da_dn": g.da_down, "db_dn": g.db_down}
+           "da_dn": g.da_down, "db_dn": g.db_down, "d_topk_w": rg.d_topk_w,
+           "d_logits": rg.d_logits}
     ref = {"y": fw["y"], "dx": bw["dx"], "da_gu": bw["da_gu"], "db_gu": bw["db_gu"],
-           "da_dn": bw["da_dn"], "db_dn": bw["db_dn"]}
+           "da_dn": bw["da_dn"], "db_dn": bw["db_dn"], "d_topk_w": rgr["d_topk_w"],
+           "d_logits": rgr["d_logits"]}
     errs = {}
     for key in got:
         a = to_numpy_f64(got[key])
@@ -76,8 +82,8 @@ def test_layer_parity(name):
         for key in ("da_gu", "db_gu", "da_dn", "db_dn"):
             assert not np.any(to_numpy_f64(got[key])[e]), (key, e)
     # bitwise reproducible
-    rt2, y2, g2 = _run(dims, logits, x, dy, w)
+    rt2, y2, g2, rg2 = _run(dims, logits, x, dy, w)
     assert torch.equal(y.view(torch.int16), y2.view(torch.int16))
-    for a, b in zip(g, g2):
+    for a, b in zip(list(g) + list(rg), list(g2) + list(rg2)):
         assert torch.equal(a.view(torch.int16) if a.dtype == torch.bfloat16 else a,
                            b.view(torch.int16) if b.dtype == torch.bfloat16 else b)

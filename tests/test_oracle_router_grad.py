@@ -118,3 +118,14 @@ def test_k_one_has_no_logit_gradient():
     assert np.all(w == 1.0)
     assert np.all(got["d_logits"] == 0.0)
     assert np.max(np.abs(got["d_topk_w"])) > 0
+
+
+def test_token_rows_match_the_whole_batch():
+    dims = _dims(n_shared=1)
+    inp = make_inputs(dims, seed=11)
+    ids, w = oracle.topk_softmax(inp.logits, dims.k)
+    full = oracle.router_grads(inp, ids, w, dims)
+    toks = [0, 5, dims.T - 1]
+    rows = oracle.router_grads_tokens(inp, ids, w, dims, toks)
+    for key in ("d_topk_w", "d_logits"):
+        assert np.max(np.abs(rows[key] - full[key][toks])) <= 1e-12 * np.max(np.abs(full[key]))
