@@ -12,6 +12,10 @@ Prints ONE JSON line.  Besides the driver's fields it carries
   gemm_mfma_frac  algorithmic grouped-GEMM FLOPs / summed GEMM kernel time /
                 bf16 dense MFMA peak;
   kernels_us    average duration per kernel;
+  router_grads  the optional routing-weight / logit gradients (the pages freeze
+                the router, so they are not part of the step): a third timed
+                region of backward calls that also produce them, its extra
+                time per step and the router_grad kernel against HBM peak;
   cpu_baseline  the CPU oracle timed on a bounded sample of the same workload.
 """
 from __future__ import annotations
@@ -66,6 +70,9 @@ def kernel_work(c):
         "grad_da_dn": (2 * P * n * r, H + R + Et * n * r * 4),
         "grad_db_gu": (2 * P * r * 2 * n, R + G + Et * r * 2 * n * 4),
         "grad_da_gu": (2 * P * d * r, X + R + Et * d * r * 4 + idx),
+        # partials per 64-column group, pair positions, weights and ids in;
+        # d_topk_w and d_logits out
+        "router_grad": (0, T * k * (n // 64) * 4 + 3 * T * k * 4 + T * k * 4 + T * c.E * 4),
     }
 
 
@@ -240,6 +247,32 @@ def main():
     for v in mem.values():
         v["frac_of_hbm_peak"] = round(v["GB/s"] * 1e9 / PEAK_HBM, 3)
 
+    # optional router gradients: backward alone, without and with them
+    def bwd_ms(router):
+        for _ in range(2):
+            layer.backward(dy, x, router=router)
+        torch.cuda.synchronize()
+        t0.record()
+        for _ in range(args.steps):
+            layer.backward(dy, x, router=router)
+        t1.record()
+        torch.cuda.synchronize()
+        return t0.elapsed_time(t1) / args.steps
+
+    b_plain, b_router = bwd_ms(False), bwd_ms(True)
+    _lib.timing_enable(True)
+    for _ in range(args.steps):
+        layer.backward(dy, x, router=True)
+    torch.cuda.synchronize()
+    rrep = _lib.timing_report()
+    _lib.timing_enable(False)
+    rg_us = 1e3 * rrep["router_grad"][0] / rrep["router_grad"][1]
+    rg_bytes = work["router_grad"][1]
+    router = {"backward_ms": round(b_plain, 4), "backward_with_router_ms": round(b_router, 4),
+              "router_grad_us": round(rg_us, 2), "router_grad_GB/s": round(rg_bytes / rg_us / 1e3, 1),
+              "router_grad_frac_of_hbm_peak": round(rg_bytes / (rg_us * 1e-6) / PEAK_HBM, 3),
+              "algorithmic_bytes": rg_bytes}
+
     out = {
         "metric": METRIC,
         "value": c.T / (ms * 1e-3),
@@ -261,6 +294,7 @@ def main():
         "roofline": roof,
         "kernels_us": {k: round(v, 2) for k, v in sorted(avg_us.items())},
         "memory_bound_kernels": mem,
+        "router_grads": router,
     }
     if args.cpu_budget > 0:
         out["cpu_baseline"] = cpu_baseline(c, inp, args.cpu_budget)
