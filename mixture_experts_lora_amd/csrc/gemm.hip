@@ -1164,6 +1164,8 @@ hipError_t gemm_dh(const Layer& L, hipStream_t st) {
 
 bool dh_writes_router_partials() { return MOE_STREAM_DH != 0; }
 
+bool prepass_writes_weighted_rows(const Layer& L) { return MOE_STREAM_PRE && L.rs <= 64; }
+
 hipError_t gemm_dx(const Layer& L, hipStream_t st) {
   using C = MainCfg<MOE_CFG_DX>::type;
   launch_prepass<PRE_QGU>(L, st, "prepass_qgu");

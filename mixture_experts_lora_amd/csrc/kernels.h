@@ -110,6 +110,9 @@ hipError_t launch_gather_table(const Layer& L, int32_t* tok, float* wgt, hipStre
 hipError_t launch_router_grad(const Layer& L, float* d_topk_w, float* d_logits, hipStream_t st);
 // Whether gemm_dh writes the <dH, H> partials (the streamed dh does).
 bool dh_writes_router_partials();
+// Whether the Q_dn pre-pass also writes w Q_dn and w (s H A_dn) (the streamed
+// pre-pass does); otherwise the LoRA gradients compute them first.
+bool prepass_writes_weighted_rows(const Layer& L);
 hipError_t launch_combine(const Layer& L, bool weighted, const bf16_t* src, bf16_t* dst,
                           hipStream_t st);
 

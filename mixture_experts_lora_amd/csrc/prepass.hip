@@ -2,7 +2,9 @@
 // low-rank path is (X A) B, never B A^T merged into W):
 //   X A_gu     out[p] = s X[tok p] A_gu[e]      (contraction d)
 //   H A_dn     out[p] = s H[p] A_dn[e]          (contraction n)
-//   Q_dn       out[p] = s dY[tok p] B_dn[e]^T   (contraction d)
+//   Q_dn       out[p] = s dY[tok p] B_dn[e]^T   (contraction d), and with it
+//              w Q_dn and w (s H A_dn), the weighted rows the down module's
+//              LoRA gradients contract with (w = routing weight of row p)
 //   Q_gu       out[p] = s dG[p] B_gu[e]^T       (contraction 2n)
 // for the expert e owning sorted row p; columns [r, rs) come out zero.
 //
@@ -39,6 +41,9 @@ static_assert(QNA * QW * 1024 == QA * 2 && QNF * 4 * 1024 == QF * 2, "panel spli
 typedef short v4s __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) v4s lds_v4s;
 typedef unsigned v2u __attribute__((ext_vector_type(2)));
+
+__device__ __forceinline__ float s_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float s_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
 
 template <int KIND>
 struct QP {
@@ -94,6 +99,9 @@ __global__ __launch_bounds__(QNT) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
   const int lf = (lane & 7) ^ (((lane >> 4) & 1) * 4);
   bf16_t* out = KIND == PRE_XA ? L.xa : KIND == PRE_HA ? L.ha : KIND == PRE_QDN ? L.qdn : L.qgu;
   const rsrc_t ro = make_rsrc(out, (int64_t)L.Ptot * rs * 2);
+  const rsrc_t rqw = make_rsrc(L.qw, (int64_t)L.Ptot * rs * 2);
+  const rsrc_t rhw = make_rsrc(L.hw, (int64_t)L.Ptot * rs * 2);
+  const rsrc_t rha = make_rsrc(L.ha, (int64_t)L.Ptot * rs * 2);
   const float sc = L.s;
 
 #pragma unroll 1
@@ -196,6 +204,10 @@ __global__ __launch_bounds__(QNT) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
     // lane: row 32 wid + lane % 32, columns 32 f + 8 g + 4 (lane / 32) + 0..3
     const int m = 32 * wid + (lane & 31);
     const int64_t p = row0 + m;
+    // Q_dn also leaves the weighted rank-r rows of the down module's LoRA
+    // gradients: w Q_dn and w (s H A_dn), each rounded from the bf16 row
+    float wr = 0.0f;
+    if constexpr (KIND == PRE_QDN) wr = m < h ? L.wgt[p] : 0.0f;
 #pragma unroll
     for (int f = 0; f < 2; ++f) {
       const f32x16& v = f ? acc1 : acc0;
@@ -205,6 +217,13 @@ __global__ __launch_bounds__(QNT) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
         const uint32_t o = m < h && c < rs ? (uint32_t)((p * rs + c) * 2) : OOB;
         const v2u w = {pack2(sc * v[4 * g], sc * v[4 * g + 1]), pack2(sc * v[4 * g + 2], sc * v[4 * g + 3])};
         __builtin_amdgcn_raw_buffer_store_b64(w, ro, o, 0, 0);
+        if constexpr (KIND == PRE_QDN) {
+          const v2u qw = {pack2(wr * s_lo(w[0]), wr * s_hi(w[0])), pack2(wr * s_lo(w[1]), wr * s_hi(w[1]))};
+          __builtin_amdgcn_raw_buffer_store_b64(qw, rqw, o, 0, 0);
+          const v2u ha = __builtin_amdgcn_raw_buffer_load_b64(rha, o, 0, 0);
+          const v2u hw = {pack2(wr * s_lo(ha[0]), wr * s_hi(ha[0])), pack2(wr * s_lo(ha[1]), wr * s_hi(ha[1]))};
+          __builtin_amdgcn_raw_buffer_store_b64(hw, rhw, o, 0, 0);
+        }
       }
     }
   }
