@@ -32,8 +32,9 @@
  *    as raw 16-bit patterns (moe_bf16).
  *  - The caller owns every buffer.  The library allocates no device memory,
  *    frees nothing and keeps no pointer after returning; its only mutable
- *    global state is the opt-in kernel-timing recorder declared at the end of
- *    this file.  Calls on different streams are independent.
+ *    global state is the opt-in kernel-timing recorder and the per-shape
+ *    engine table, both declared at the end of this file.  Calls on
+ *    different streams are independent.
  *  - Inputs are never written.  Outputs must not alias inputs or each other.
  *  - Outputs are overwritten, never accumulated into (an expert that receives
  *    no rows gets exactly zero LoRA gradients).
@@ -164,8 +165,8 @@ moe_status moe_lora_forward(const moe_dims* dims, const moe_bf16* x, const moe_r
  *              experts not selected (the selection is locally constant); the
  *              shared expert's weight is the constant 1 and takes none.
  *              For models that train the router (the pages freeze it).
- *              MOE_ERROR_UNSUPPORTED if this build's dh kernel cannot supply
- *              the dot products.
+ *              They come from the streamed dh kernel, which this call then
+ *              uses whatever engine is set for the shape.
  *   ws   scratch of moe_workspace_bytes(dims) */
 moe_status moe_lora_backward(const moe_dims* dims, const moe_bf16* dy, const moe_bf16* x,
                              const moe_routing* routing, const moe_weights* weights,
@@ -173,6 +174,42 @@ moe_status moe_lora_backward(const moe_dims* dims, const moe_bf16* dy, const moe
                              float* da_gate_up, float* db_gate_up, float* da_down,
                              float* db_down, float* d_topk_w, float* d_logits, void* ws,
                              size_t ws_bytes, void* stream);
+
+/* Engines.  Every grouped product has two implementations: register-path
+ * kernels (global -> registers -> LDS) and streamed ones (global -> LDS by
+ * buffer_load ... lds through a ring, one persistent workgroup per CU).  Which
+ * runs is chosen per layer shape (d, n, E, k, r, n_shared; not T), process-
+ * wide, by these bits (set = streamed):
+ *   MOE_ENGINE_GATE_UP, MOE_ENGINE_DOWN, MOE_ENGINE_DH, MOE_ENGINE_DX  the
+ *     four grouped GEMMs;
+ *   MOE_ENGINE_RANK  the rank-r pre-passes and the LoRA gradients (r <= 64;
+ *     above that both settings use the register path).
+ * Without a recorded choice a shape uses the build's defaults (everything
+ * streamed except gate_up).
+ * moe_set_engines records a choice (MOE_ERROR_INVALID_VALUE for unknown bits);
+ * moe_get_engines returns the choice in force.  Results agree between engines
+ * to the layer's tolerance, not bitwise.
+ * moe_autotune is the one-time start-up autotune of the faster-MoE page's
+ * kernels ("Unsloth MoE Triton kernels"), cached per shape: it runs route +
+ * forward + backward on the given inputs once per setting (all streamed, all
+ * register-path; one warm-up and three timed steps each, every kernel timed
+ * with events), keeps per product the faster engine, records and returns the
+ * choice.  Unlike every other entry point it waits for the GPU; it also
+ * switches the kernel-timing recorder off.  scratch: device memory of at
+ * least moe_autotune_scratch_bytes(dims), 256-byte aligned, for all the
+ * routing, saved, workspace and output buffers of those steps; its contents
+ * are undefined afterwards.  logits, x, dy, weights as for the other calls. */
+#define MOE_ENGINE_GATE_UP 1u
+#define MOE_ENGINE_DOWN 2u
+#define MOE_ENGINE_DH 4u
+#define MOE_ENGINE_DX 8u
+#define MOE_ENGINE_RANK 16u
+moe_status moe_set_engines(const moe_dims* dims, unsigned engines);
+unsigned moe_get_engines(const moe_dims* dims);
+size_t moe_autotune_scratch_bytes(const moe_dims* dims);
+moe_status moe_autotune(const moe_dims* dims, const float* logits, const moe_bf16* x,
+                        const moe_bf16* dy, const moe_weights* weights, void* scratch,
+                        size_t scratch_bytes, void* stream, unsigned* engines_out);
 
 /* Kernel timing, for measurement tools (not part of the layer's math).
  * moe_timing_enable(1) starts recording: every kernel the library enqueues

@@ -6,20 +6,29 @@ tensors.  Importing the package does not load the library; the first call
 does, and fails loudly if it has not been built.
 """
 from .api import (  # noqa: F401
+    ENGINE_ALL,
+    ENGINE_DH,
+    ENGINE_DOWN,
+    ENGINE_DX,
+    ENGINE_GATE_UP,
+    ENGINE_RANK,
     Dims,
     Grads,
     MoELoRALayer,
     RouterGrads,
     Routing,
     Weights,
+    autotune,
     backward,
     empty_grads,
     empty_router_grads,
     empty_routing,
     forward,
     forward_saved_bytes,
+    get_engines,
     route,
     route_workspace_bytes,
+    set_engines,
     workspace_bytes,
 )
 from ._lib import MoeError, load  # noqa: F401

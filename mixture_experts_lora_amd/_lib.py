@@ -21,6 +21,10 @@ EXPORTED = (
     "moe_route",
     "moe_lora_forward",
     "moe_lora_backward",
+    "moe_set_engines",
+    "moe_get_engines",
+    "moe_autotune_scratch_bytes",
+    "moe_autotune",
     "moe_timing_enable",
     "moe_timing_report",
 )
@@ -75,6 +79,14 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.moe_lora_forward.argtypes = [pd, vp, pr, pw, vp, vp, sz, vp, sz, vp]
     lib.moe_lora_backward.restype = ctypes.c_int
     lib.moe_lora_backward.argtypes = [pd, vp, vp, pr, pw, vp, sz, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
+    lib.moe_set_engines.restype = ctypes.c_int
+    lib.moe_set_engines.argtypes = [pd, ctypes.c_uint]
+    lib.moe_get_engines.restype = ctypes.c_uint
+    lib.moe_get_engines.argtypes = [pd]
+    lib.moe_autotune_scratch_bytes.restype = sz
+    lib.moe_autotune_scratch_bytes.argtypes = [pd]
+    lib.moe_autotune.restype = ctypes.c_int
+    lib.moe_autotune.argtypes = [pd, vp, vp, vp, pw, vp, sz, vp, ctypes.POINTER(ctypes.c_uint)]
     lib.moe_timing_enable.restype = ctypes.c_int
     lib.moe_timing_enable.argtypes = [ctypes.c_int]
     lib.moe_timing_report.restype = ctypes.c_int

@@ -240,6 +240,41 @@ def backward(dy: torch.Tensor, x: torch.Tensor, routing: Routing, weights: Weigh
     return out
 
 
+ENGINE_GATE_UP, ENGINE_DOWN, ENGINE_DH, ENGINE_DX, ENGINE_RANK = 1, 2, 4, 8, 16
+ENGINE_ALL = 31
+
+
+def set_engines(dims: Dims, engines: int) -> None:
+    """Record the engines for this layer shape (bit set = streamed kernels)."""
+    lib = _lib.load()
+    dc = dims.c()
+    _lib.check(lib.moe_set_engines(ctypes.byref(dc), int(engines)), "moe_set_engines")
+
+
+def get_engines(dims: Dims) -> int:
+    lib = _lib.load()
+    dc = dims.c()
+    return int(lib.moe_get_engines(ctypes.byref(dc)))
+
+
+def autotune(dims: Dims, logits: torch.Tensor, x: torch.Tensor, dy: torch.Tensor,
+             weights: Weights, stream=None) -> int:
+    """One-time per-shape engine autotune (waits for the GPU); returns and
+    records the chosen engine bits."""
+    lib = _lib.load()
+    _check(logits, (dims.T, dims.E), torch.float32, "logits")
+    _check(x, (dims.T, dims.d), torch.bfloat16, "x")
+    _check(dy, (dims.T, dims.d), torch.bfloat16, "dy")
+    _check_weights(weights, dims)
+    dc, wc = dims.c(), _c_weights(weights)
+    scratch = _bytes(int(lib.moe_autotune_scratch_bytes(ctypes.byref(dc))), x.device)
+    out = ctypes.c_uint(0)
+    _lib.check(lib.moe_autotune(ctypes.byref(dc), logits.data_ptr(), x.data_ptr(), dy.data_ptr(),
+                                ctypes.byref(wc), scratch.data_ptr(), scratch.numel(),
+                                _stream(stream), ctypes.byref(out)), "moe_autotune")
+    return int(out.value)
+
+
 class MoELoRALayer:
     """One layer with every buffer allocated up front, so that route / forward /
     backward allocate nothing per call (the benchmark's steady state)."""

@@ -17,7 +17,7 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 OBJ = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libmoe_lora.so")
-SOURCES = ("api.hip", "route.hip", "gemm.hip", "stream.hip", "prepass.hip", "grads.hip", "layer.hip", "timing.hip")
+SOURCES = ("api.hip", "route.hip", "gemm.hip", "stream.hip", "prepass.hip", "grads.hip", "layer.hip", "tune.hip", "timing.hip")
 ARCH = "gfx950"
 
 HIPCC_FLAGS = [

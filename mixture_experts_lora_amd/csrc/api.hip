@@ -43,6 +43,7 @@ Layer make_layer(const moe_dims* dm) {
   L.Ptot = L.P + L.S * L.T;
   L.s = dm->lora_scale;
   L.ncu = device_cu_count();
+  L.engines = lookup_engines(dm->d, dm->n, dm->E, dm->k, dm->r, dm->n_shared);
   return L;
 }
 
@@ -199,7 +200,6 @@ moe_status moe_lora_backward(const moe_dims* dm, const moe_bf16* dy, const moe_b
   if ((d_topk_w && !aligned16(d_topk_w)) || (d_logits && !aligned16(d_logits)))
     return MOE_ERROR_INVALID_VALUE;
   const bool router = d_topk_w || d_logits;
-  if (router && !dh_writes_router_partials()) return MOE_ERROR_UNSUPPORTED;
   if (saved_bytes < moe_forward_saved_bytes(dm) || ws_bytes < moe_workspace_bytes(dm))
     return MOE_ERROR_WORKSPACE;
   hipStream_t s = (hipStream_t)stream;
@@ -213,9 +213,12 @@ moe_status moe_lora_backward(const moe_dims* dm, const moe_bf16* dy, const moe_b
   L.db_gu = db_gate_up;
   L.da_dn = da_down;
   L.db_dn = db_down;
-  if (router)
+  if (router) {
+    // the <dH, H> partials come from the streamed dh's epilogue
+    L.engines |= ENG_DH_STREAM;
     L.dw_part = (float*)((char*)ws + ws_layout(dm->T, dm->d, dm->n, dm->E, dm->k, dm->r,
                                                dm->n_shared).dw_part);
+  }
   hipError_t e = maybe_pack(L, w, s);
   if (e == hipSuccess) e = gemm_dh(L, s);
   if (e == hipSuccess && router) e = launch_router_grad(L, d_topk_w, d_logits, s);

@@ -1112,7 +1112,7 @@ static int mtiles_bound(const Layer& L, int BM) { return L.Ptot / BM + L.Et; }
 
 template <int KIND>
 static void launch_prepass(const Layer& L, hipStream_t st, const char* name) {
-  if (MOE_STREAM_PRE && L.rs <= 64) {
+  if ((L.engines & ENG_RANK_STREAM) && L.rs <= 64) {
     stream_prepass(L, KIND, st);
     return;
   }
@@ -1137,7 +1137,7 @@ static void launch_prepass(const Layer& L, hipStream_t st, const char* name) {
 hipError_t gemm_gate_up(const Layer& L, hipStream_t st) {
   using C = MainCfg<MOE_CFG_GU>::type;
   launch_prepass<PRE_XA>(L, st, "prepass_xa");
-  if (MOE_STREAM_GU) return stream_gate_up(L, st);
+  if (L.engines & ENG_GU_STREAM) return stream_gate_up(L, st);
   const int tiles = mtiles_bound(L, C::BM) * cdiv(L.n, C::BN / 2);
   MOE_LAUNCH("gate_up", k_gate_up<C>, dim3(grid_for(tiles, wg_per_cu<C>(), L.ncu)), dim3(C::NT), 0,
              st, L);
@@ -1147,7 +1147,7 @@ hipError_t gemm_gate_up(const Layer& L, hipStream_t st) {
 hipError_t gemm_down(const Layer& L, hipStream_t st) {
   using C = MainCfg<MOE_CFG_DN>::type;
   launch_prepass<PRE_HA>(L, st, "prepass_ha");
-  if (MOE_STREAM_DN) return stream_down(L, st);
+  if (L.engines & ENG_DN_STREAM) return stream_down(L, st);
   const int tiles = mtiles_bound(L, C::BM) * cdiv(L.d, C::BN);
   MOE_LAUNCH("down", k_down<C>, dim3(grid_for(tiles, wg_per_cu<C>(), L.ncu)), dim3(C::NT), 0, st, L);
   return hipGetLastError();
@@ -1156,20 +1156,24 @@ hipError_t gemm_down(const Layer& L, hipStream_t st) {
 hipError_t gemm_dh(const Layer& L, hipStream_t st) {
   using C = MainCfg<MOE_CFG_DH>::type;
   launch_prepass<PRE_QDN>(L, st, "prepass_qdn");
-  if (MOE_STREAM_DH) return stream_dh(L, st);
+  if (L.engines & ENG_DH_STREAM) return stream_dh(L, st);
   const int tiles = mtiles_bound(L, C::BM) * cdiv(L.n, C::BN);
   MOE_LAUNCH("dh", k_dh<C>, dim3(grid_for(tiles, wg_per_cu<C>(), L.ncu)), dim3(C::NT), 0, st, L);
   return hipGetLastError();
 }
 
-bool dh_writes_router_partials() { return MOE_STREAM_DH != 0; }
+uint32_t default_engines() {
+  return (MOE_STREAM_GU ? ENG_GU_STREAM : 0u) | (MOE_STREAM_DN ? ENG_DN_STREAM : 0u) |
+         (MOE_STREAM_DH ? ENG_DH_STREAM : 0u) | (MOE_STREAM_DX ? ENG_DX_STREAM : 0u) |
+         (MOE_STREAM_PRE ? ENG_RANK_STREAM : 0u);
+}
 
-bool prepass_writes_weighted_rows(const Layer& L) { return MOE_STREAM_PRE && L.rs <= 64; }
+bool prepass_writes_weighted_rows(const Layer& L) { return (L.engines & ENG_RANK_STREAM) && L.rs <= 64; }
 
 hipError_t gemm_dx(const Layer& L, hipStream_t st) {
   using C = MainCfg<MOE_CFG_DX>::type;
   launch_prepass<PRE_QGU>(L, st, "prepass_qgu");
-  if (MOE_STREAM_DX) return stream_dx(L, st);
+  if (L.engines & ENG_DX_STREAM) return stream_dx(L, st);
   const int tiles = mtiles_bound(L, C::BM) * cdiv(L.d, C::BN);
   MOE_LAUNCH("dx", k_dx<C>, dim3(grid_for(tiles, wg_per_cu<C>(), L.ncu)), dim3(C::NT), 0, st, L);
   return hipGetLastError();
@@ -1205,13 +1209,9 @@ template <> struct GradCfgA<4> { using type = Cfg<128, 64, 4, 1, 1>; };
 #define MOE_GRAD_A 0
 #endif
 
-// 1: rank <= 64 gradients on the LDS-DMA kernels of grads.hip
-#ifndef MOE_DMA_GRADS
-#define MOE_DMA_GRADS 1
-#endif
 
 hipError_t gemm_lora_grads(const Layer& L, hipStream_t st) {
-  if (MOE_DMA_GRADS && L.rs <= 64) {
+  if ((L.engines & ENG_RANK_STREAM) && L.rs <= 64) {
     const hipError_t e = dma_lora_grads(L, st);
     if (e != hipSuccess) return e;
   } else if (L.rs <= 64) {

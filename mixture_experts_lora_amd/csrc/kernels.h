@@ -13,8 +13,20 @@ typedef uint16_t bf16_t;
 // Rows of every grouped GEMM are "sorted positions" p in [0, P_tot): routed
 // pairs in expert order p < P (expert e owns [offsets[e], offsets[e+1])),
 // then the shared expert's T rows p = P + t.
+// Engine of each product (bit set = streamed / one-launch LDS-DMA engine,
+// clear = register-path engine); the choice is made per layer shape.
+enum EngineBits : uint32_t {
+  ENG_GU_STREAM = 1u << 0,    // gate_up grouped GEMM
+  ENG_DN_STREAM = 1u << 1,    // down
+  ENG_DH_STREAM = 1u << 2,    // dh (+ SwiGLU backward); router-gradient partials need it
+  ENG_DX_STREAM = 1u << 3,    // dX per pair
+  ENG_RANK_STREAM = 1u << 4,  // rank-r pre-passes and LoRA gradients (rank <= 64)
+  ENG_ALL = 31u
+};
+
 struct Layer {
   int T, d, n, E, k, r, S, Et;
+  uint32_t engines;  // EngineBits
   int rs;       // row stride of the rank-r activations (r rounded up to 8)
   int ra;       // row stride used to read A_gu / A_dn (r, or rs for the packed copies)
   int P, Ptot;  // routed pairs, all rows
@@ -109,10 +121,14 @@ hipError_t launch_gather_table(const Layer& L, int32_t* tok, float* wgt, hipStre
 // Routing-weight and logit gradients from the dh epilogue's partials.
 hipError_t launch_router_grad(const Layer& L, float* d_topk_w, float* d_logits, hipStream_t st);
 // Whether gemm_dh writes the <dH, H> partials (the streamed dh does).
-bool dh_writes_router_partials();
+// The engines this build uses when nothing else was chosen for a shape.
+uint32_t default_engines();
 // Whether the Q_dn pre-pass also writes w Q_dn and w (s H A_dn) (the streamed
 // pre-pass does); otherwise the LoRA gradients compute them first.
 bool prepass_writes_weighted_rows(const Layer& L);
+// Shape -> engines table (api.hip): a recorded choice, else default_engines().
+uint32_t lookup_engines(int d, int n, int E, int k, int r, int S);
+void record_engines(int d, int n, int E, int k, int r, int S, uint32_t engines);
 hipError_t launch_combine(const Layer& L, bool weighted, const bf16_t* src, bf16_t* dst,
                           hipStream_t st);
 

@@ -122,3 +122,26 @@ def test_python_binding_refuses_cpu_tensors():
     dims = mel.Dims(T=4, d=64, n=64, E=2, k=1, r=4)
     with pytest.raises(ValueError):
         mel.route(torch.zeros(4, 2), dims)
+
+
+def test_engine_table_on_the_host(lib):
+    dm = _lib.MoeDims(T=64, d=128, n=64, E=8, k=2, r=4, n_shared=0, lora_scale=1.0)
+    default = lib.moe_get_engines(ctypes.byref(dm))
+    assert 0 <= default <= 31
+    assert lib.moe_set_engines(ctypes.byref(dm), 32) == 1          # unknown bit
+    assert lib.moe_set_engines(ctypes.byref(dm), 5) == 0
+    assert lib.moe_get_engines(ctypes.byref(dm)) == 5
+    other = _lib.MoeDims(T=64, d=128, n=64, E=8, k=2, r=8, n_shared=0, lora_scale=1.0)
+    assert lib.moe_get_engines(ctypes.byref(other)) == default      # another shape
+    dm.T = 999                                                       # T is not part of the key
+    assert lib.moe_get_engines(ctypes.byref(dm)) == 5
+    assert lib.moe_set_engines(ctypes.byref(dm), default) == 0
+    # autotune validates on the host before touching the GPU
+    need = lib.moe_autotune_scratch_bytes(ctypes.byref(dm))
+    assert need > lib.moe_workspace_bytes(ctypes.byref(dm))
+    w = _lib.MoeWeights(*([256] * 6))
+    out = ctypes.c_uint(0)
+    assert lib.moe_autotune(ctypes.byref(dm), 256, 256, 256, ctypes.byref(w), 256, need - 1, None,
+                            ctypes.byref(out)) == 3
+    assert lib.moe_autotune(ctypes.byref(dm), 256, 256, 256, ctypes.byref(w), 128, need, None,
+                            ctypes.byref(out)) == 1

@@ -87,3 +87,62 @@ def test_layer_parity(name):
     for a, b in zip(list(g) + list(rg), list(g2) + list(rg2)):
         assert torch.equal(a.view(torch.int16) if a.dtype == torch.bfloat16 else a,
                            b.view(torch.int16) if b.dtype == torch.bfloat16 else b)
+
+
+ENGINE_CASES = ["tiny", "ragged_shared_r3_s2", "r128_n192", "empty_experts_r64", "splitk_two_chunks",
+                "wide_d320_zipf"]
+
+
+@pytest.mark.parametrize("engines", [0, mel.ENGINE_ALL], ids=["register_path", "streamed"])
+@pytest.mark.parametrize("name", ENGINE_CASES)
+def test_layer_parity_each_engine(name, engines):
+    """Every product on one engine: all register-path kernels, or all streamed."""
+    require_gpu()
+    ld = CASES[name]
+    announce("engines", f"{name} engines={engines}", ld)
+    inp = make_inputs(ld, seed=2)
+    dims = mdims(ld)
+    logits, x, dy, w = upload(inp)
+    before = mel.get_engines(dims)
+    mel.set_engines(dims, engines)
+    try:
+        assert mel.get_engines(dims) == engines
+        rt, y, g, rg = _run(dims, logits, x, dy, w)
+    finally:
+        mel.set_engines(dims, before)
+    ids = rt.topk_ids.cpu().numpy()
+    tw = rt.topk_w.cpu().numpy()
+    fw = oracle.forward(inp, ids, tw, ld)
+    bw = oracle.backward(inp, ids, tw, ld)
+    rgr = oracle.router_grads(inp, ids, tw, ld)
+    pairs = [(y, fw["y"]), (g.dx, bw["dx"]), (g.da_gate_up, bw["da_gu"]), (g.db_gate_up, bw["db_gu"]),
+             (g.da_down, bw["da_dn"]), (g.db_down, bw["db_dn"]), (rg.d_topk_w, rgr["d_topk_w"]),
+             (rg.d_logits, rgr["d_logits"])]
+    errs = [relerr(to_numpy_f64(a), b) for a, b in pairs]
+    print("errors", " ".join(f"{e:.2e}" for e in errs), flush=True)
+    assert max(errs) <= TOL
+
+
+def test_autotune_records_a_choice_that_keeps_parity():
+    require_gpu()
+    ld = LayerDims(2048, 256, 128, 16, 4, 16)
+    announce("autotune", "T2048_d256_n128_E16_k4_r16", ld)
+    inp = make_inputs(ld, seed=4)
+    dims = mdims(ld)
+    logits, x, dy, w = upload(inp)
+    before = mel.get_engines(dims)
+    try:
+        chosen = mel.autotune(dims, logits, x, dy, w)
+        print("chosen engines", chosen, flush=True)
+        assert 0 <= chosen <= mel.ENGINE_ALL
+        assert mel.get_engines(dims) == chosen
+        rt, y, g, rg = _run(dims, logits, x, dy, w)
+    finally:
+        mel.set_engines(dims, before)
+    ids = rt.topk_ids.cpu().numpy()
+    tw = rt.topk_w.cpu().numpy()
+    fw = oracle.forward(inp, ids, tw, ld)
+    bw = oracle.backward(inp, ids, tw, ld)
+    assert relerr(to_numpy_f64(y), fw["y"]) <= TOL
+    assert relerr(to_numpy_f64(g.dx), bw["dx"]) <= TOL
+    assert relerr(to_numpy_f64(g.da_gate_up), bw["da_gu"]) <= TOL
