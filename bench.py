@@ -16,6 +16,8 @@ Prints ONE JSON line.  Besides the driver's fields it carries
                 the router, so they are not part of the step): a third timed
                 region of backward calls that also produce them, its extra
                 time per step and the router_grad kernel against HBM peak;
+  engines       the engine of each product (the one-time autotune's choice,
+                made before the warm-up steps, unless --no-autotune);
   cpu_baseline  the CPU oracle timed on a bounded sample of the same workload.
 """
 from __future__ import annotations
@@ -145,6 +147,8 @@ def main():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--config", default="qwen3_30b_a3b")
+    ap.add_argument("--no-autotune", action="store_true",
+                    help="keep the build's default engines instead of the one-time autotune")
     ap.add_argument("--cpu-budget", type=float, default=10.0,
                     help="seconds of CPU oracle work for cpu_baseline (0 = skip)")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
@@ -193,6 +197,9 @@ def main():
     logits = torch.from_numpy(inp.logits).cuda()
     x, dy = bf(inp.x), bf(inp.dy)
     layer = mel.MoELoRALayer(dims, w)
+    # one-time per-shape engine autotune before any timed step (untimed, as
+    # the start-up autotune of the pages' kernels)
+    engines = mel.get_engines(dims) if args.no_autotune else mel.autotune(dims, logits, x, dy, w)
 
     def step():
         layer.route(logits)
@@ -300,6 +307,11 @@ def main():
         "kernels_us": {k: round(v, 2) for k, v in sorted(avg_us.items())},
         "memory_bound_kernels": mem,
         "router_grads": router,
+        "engines": {"bits": engines, "autotuned": not args.no_autotune,
+                    **{name: "streamed" if engines & bit else "register-path" for name, bit in
+                       (("gate_up", mel.ENGINE_GATE_UP), ("down", mel.ENGINE_DOWN),
+                        ("dh", mel.ENGINE_DH), ("dx", mel.ENGINE_DX),
+                        ("rank_r", mel.ENGINE_RANK))}},
     }
     if args.cpu_budget > 0:
         out["cpu_baseline"] = cpu_baseline(c, inp, args.cpu_budget)
