@@ -23,6 +23,7 @@ Prints ONE JSON line.  Besides the driver's fields it carries
 from __future__ import annotations
 
 import argparse
+import dataclasses
 import json
 import os
 import sys
@@ -147,6 +148,8 @@ def main():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--config", default="qwen3_30b_a3b")
+    ap.add_argument("--dtype", choices=("bf16", "f16"), default="bf16",
+                    help="16-bit element type of activations and weights")
     ap.add_argument("--no-autotune", action="store_true",
                     help="keep the build's default engines instead of the one-time autotune")
     ap.add_argument("--cpu-budget", type=float, default=10.0,
@@ -185,12 +188,13 @@ def main():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(1)
     mel.load()
-    c = CONFIGS[args.config]
+    c = dataclasses.replace(CONFIGS[args.config], element=args.dtype)
     inp = make_inputs(c, seed=0)
-    dims = mel.Dims(c.T, c.d, c.n, c.E, c.k, c.r, c.n_shared, c.lora_scale)
+    dims = mel.Dims(c.T, c.d, c.n, c.E, c.k, c.r, c.n_shared, c.lora_scale,
+                    mel.MOE_F16 if args.dtype == "f16" else mel.MOE_BF16)
 
     def bf(a):
-        return torch.from_numpy(a.view(np.int16)).cuda().view(torch.bfloat16)
+        return torch.from_numpy(a.view(np.int16)).cuda().view(dims.elem)
 
     w = mel.Weights(bf(inp.w_gu), bf(inp.w_dn), bf(inp.a_gu), bf(inp.b_gu), bf(inp.a_dn),
                     bf(inp.b_dn))
@@ -241,7 +245,8 @@ def main():
         roof = {"bound": "mfma", "achieved": f / t_dom / 1e12, "peak": PEAK_BF16 / 1e12,
                 "unit": "TFLOP/s"}
     roof["frac"] = roof["achieved"] / roof["peak"]
-    roof["traffic"] = measured_traffic(dom, args.config)
+    roof["traffic"] = measured_traffic(dom, args.config if args.dtype == "bf16"
+                                       else f"{args.config}_{args.dtype}")
     roof["kernel"] = dom
     roof["kernel_us"] = avg_us[dom]
     roof["algorithmic_bytes"] = byts
@@ -296,7 +301,7 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "bf16",
+        "dtype": args.dtype,
         "data": "synthetic (seeded normal draws; no dataset, random-init weights)",
         "config": {"workload": f"{c.name}: MoE-LoRA expert layer route+fwd+bwd", "T": c.T,
                    "d": c.d, "n": c.n, "E": c.E, "top_k": c.k, "lora_rank": c.r,

@@ -28,8 +28,9 @@
  *
  * Conventions for every entry point
  *  - All tensor pointers are DEVICE pointers (hipMalloc'd or torch CUDA
- *    tensors), contiguous, row-major, 16-byte aligned.  bf16 tensors are passed
- *    as raw 16-bit patterns (moe_bf16).
+ *    tensors), contiguous, row-major, 16-byte aligned.  16-bit tensors are
+ *    passed as raw 16-bit patterns (moe_bf16; fp16 bits when dims->dtype is
+ *    MOE_F16).
  *  - The caller owns every buffer.  The library allocates no device memory,
  *    frees nothing and keeps no pointer after returning; its only mutable
  *    global state is the opt-in kernel-timing recorder and the per-shape
@@ -71,13 +72,20 @@ typedef enum {
 
 /* Layer shape.  T tokens, hidden size d, expert intermediate size n, E routed
  * experts, top-k, LoRA rank r, n_shared shared experts (0 or 1, stacked after
- * the routed ones), LoRA scale s applied to the low-rank term.
+ * the routed ones), LoRA scale s applied to the low-rank term, and the element
+ * type of every 16-bit tensor below (x, y, dy, dx, the weights and LoRA
+ * factors, and the saved activations): MOE_BF16 (0) or MOE_F16 (1, the
+ * faster-MoE page's fp16 variant of the grouped GEMM for GPUs without bf16).
+ * Logits, routing weights, accumulation and the LoRA gradients stay fp32.
  * Derived: P = T*k routed pairs; P_tot = P + n_shared*T rows of every grouped
  * GEMM; E_tot = E + n_shared stacked experts. */
+#define MOE_BF16 0
+#define MOE_F16 1
 typedef struct {
   int64_t T;
   int32_t d, n, E, k, r, n_shared;
   float lora_scale;
+  int32_t dtype;
 } moe_dims;
 
 /* Routing tensors, written by moe_route and read by forward/backward.
@@ -179,7 +187,7 @@ moe_status moe_lora_backward(const moe_dims* dims, const moe_bf16* dy, const moe
  * kernels (global -> registers -> LDS) and streamed ones (global -> LDS by
  * buffer_load ... lds through a ring, one persistent workgroup per CU).  Which
  * runs is chosen per layer shape (d, n, E, k, r, n_shared; not T), process-
- * wide, by these bits (set = streamed):
+ * wide (and per element type), by these bits (set = streamed):
  *   MOE_ENGINE_GATE_UP, MOE_ENGINE_DOWN, MOE_ENGINE_DH, MOE_ENGINE_DX  the
  *     four grouped GEMMs;
  *   MOE_ENGINE_RANK  the rank-r pre-passes and the LoRA gradients (r <= 64;

@@ -31,4 +31,4 @@ from .api import (  # noqa: F401
     set_engines,
     workspace_bytes,
 )
-from ._lib import MoeError, load  # noqa: F401
+from ._lib import MOE_BF16, MOE_F16, MoeError, load  # noqa: F401

@@ -13,6 +13,9 @@ MOE_ERROR_UNSUPPORTED = 2
 MOE_ERROR_WORKSPACE = 3
 MOE_ERROR_LAUNCH = 4
 
+MOE_BF16 = 0
+MOE_F16 = 1
+
 EXPORTED = (
     "moe_status_string",
     "moe_route_workspace_bytes",
@@ -33,7 +36,8 @@ EXPORTED = (
 class MoeDims(ctypes.Structure):
     _fields_ = [("T", ctypes.c_int64), ("d", ctypes.c_int32), ("n", ctypes.c_int32),
                 ("E", ctypes.c_int32), ("k", ctypes.c_int32), ("r", ctypes.c_int32),
-                ("n_shared", ctypes.c_int32), ("lora_scale", ctypes.c_float)]
+                ("n_shared", ctypes.c_int32), ("lora_scale", ctypes.c_float),
+                ("dtype", ctypes.c_int32)]
 
 
 class MoeRouting(ctypes.Structure):

@@ -24,6 +24,16 @@ class Dims:
     r: int
     n_shared: int = 0
     lora_scale: float = 1.0
+    dtype: int = _lib.MOE_BF16  # element type of x, y, dy, dx and the weights
+
+    @property
+    def elem(self) -> torch.dtype:
+        """torch dtype of the 16-bit tensors (activations and weights)."""
+        if self.dtype == _lib.MOE_BF16:
+            return torch.bfloat16
+        if self.dtype == _lib.MOE_F16:
+            return torch.float16
+        raise ValueError(f"unknown element type {self.dtype}")
 
     @property
     def P(self) -> int:
@@ -39,7 +49,7 @@ class Dims:
 
     def c(self) -> _lib.MoeDims:
         return _lib.MoeDims(self.T, self.d, self.n, self.E, self.k, self.r, self.n_shared,
-                            float(self.lora_scale))
+                            float(self.lora_scale), int(self.dtype))
 
 
 class Routing(NamedTuple):
@@ -52,16 +62,17 @@ class Routing(NamedTuple):
 
 
 class Weights(NamedTuple):
-    w_gate_up: torch.Tensor  # bf16 [E_tot, 2n, d]
-    w_down: torch.Tensor     # bf16 [E_tot, d, n]
-    a_gate_up: torch.Tensor  # bf16 [E_tot, d, r]
-    b_gate_up: torch.Tensor  # bf16 [E_tot, r, 2n]
-    a_down: torch.Tensor     # bf16 [E_tot, n, r]
-    b_down: torch.Tensor     # bf16 [E_tot, r, d]
+    """Frozen base weights and LoRA factors, all of the layer's element type."""
+    w_gate_up: torch.Tensor  # [E_tot, 2n, d]
+    w_down: torch.Tensor     # [E_tot, d, n]
+    a_gate_up: torch.Tensor  # [E_tot, d, r]
+    b_gate_up: torch.Tensor  # [E_tot, r, 2n]
+    a_down: torch.Tensor     # [E_tot, n, r]
+    b_down: torch.Tensor     # [E_tot, r, d]
 
 
 class Grads(NamedTuple):
-    dx: torch.Tensor          # bf16 [T, d]
+    dx: torch.Tensor          # element type [T, d]
     da_gate_up: torch.Tensor  # fp32 [E_tot, d, r]
     db_gate_up: torch.Tensor  # fp32 [E_tot, r, 2n]
     da_down: torch.Tensor     # fp32 [E_tot, n, r]
@@ -144,7 +155,7 @@ def _check_routing(rt: Routing, dims: Dims) -> None:
 
 
 def _check_weights(w: Weights, dims: Dims) -> None:
-    bf, Et, d, n, r = torch.bfloat16, dims.E_tot, dims.d, dims.n, dims.r
+    bf, Et, d, n, r = dims.elem, dims.E_tot, dims.d, dims.n, dims.r
     _check(w.w_gate_up, (Et, 2 * n, d), bf, "w_gate_up")
     _check(w.w_down, (Et, d, n), bf, "w_down")
     _check(w.a_gate_up, (Et, d, r), bf, "a_gate_up")
@@ -173,11 +184,11 @@ def forward(x: torch.Tensor, routing: Routing, weights: Weights, dims: Dims,
             ws: Optional[torch.Tensor] = None, stream=None):
     """moe_lora_forward.  Returns (y, saved); keep `saved` for backward."""
     lib = _lib.load()
-    _check(x, (dims.T, dims.d), torch.bfloat16, "x")
+    _check(x, (dims.T, dims.d), dims.elem, "x")
     _check_routing(routing, dims)
     _check_weights(weights, dims)
     y = y if y is not None else torch.empty_like(x)
-    _check(y, (dims.T, dims.d), torch.bfloat16, "y")
+    _check(y, (dims.T, dims.d), dims.elem, "y")
     if saved is None:
         saved = _bytes(forward_saved_bytes(dims), x.device)
     if ws is None:
@@ -192,7 +203,7 @@ def forward(x: torch.Tensor, routing: Routing, weights: Weights, dims: Dims,
 
 def empty_grads(dims: Dims, device) -> Grads:
     f32, Et, d, n, r = torch.float32, dims.E_tot, dims.d, dims.n, dims.r
-    return Grads(torch.empty(dims.T, d, dtype=torch.bfloat16, device=device),
+    return Grads(torch.empty(dims.T, d, dtype=dims.elem, device=device),
                  torch.empty(Et, d, r, dtype=f32, device=device),
                  torch.empty(Et, r, 2 * n, dtype=f32, device=device),
                  torch.empty(Et, n, r, dtype=f32, device=device),
@@ -211,13 +222,13 @@ def backward(dy: torch.Tensor, x: torch.Tensor, routing: Routing, weights: Weigh
     """moe_lora_backward: dX and the LoRA-factor gradients; with ``router_out``
     also the routing-weight and logit gradients (written into it)."""
     lib = _lib.load()
-    _check(dy, (dims.T, dims.d), torch.bfloat16, "dy")
-    _check(x, (dims.T, dims.d), torch.bfloat16, "x")
+    _check(dy, (dims.T, dims.d), dims.elem, "dy")
+    _check(x, (dims.T, dims.d), dims.elem, "x")
     _check_routing(routing, dims)
     _check_weights(weights, dims)
     out = out if out is not None else empty_grads(dims, dy.device)
     Et, d, n, r = dims.E_tot, dims.d, dims.n, dims.r
-    _check(out.dx, (dims.T, d), torch.bfloat16, "dx")
+    _check(out.dx, (dims.T, d), dims.elem, "dx")
     _check(out.da_gate_up, (Et, d, r), torch.float32, "da_gate_up")
     _check(out.db_gate_up, (Et, r, 2 * n), torch.float32, "db_gate_up")
     _check(out.da_down, (Et, n, r), torch.float32, "da_down")
@@ -263,8 +274,8 @@ def autotune(dims: Dims, logits: torch.Tensor, x: torch.Tensor, dy: torch.Tensor
     records the chosen engine bits."""
     lib = _lib.load()
     _check(logits, (dims.T, dims.E), torch.float32, "logits")
-    _check(x, (dims.T, dims.d), torch.bfloat16, "x")
-    _check(dy, (dims.T, dims.d), torch.bfloat16, "dy")
+    _check(x, (dims.T, dims.d), dims.elem, "x")
+    _check(dy, (dims.T, dims.d), dims.elem, "dy")
     _check_weights(weights, dims)
     dc, wc = dims.c(), _c_weights(weights)
     scratch = _bytes(int(lib.moe_autotune_scratch_bytes(ctypes.byref(dc))), x.device)
@@ -286,7 +297,7 @@ class MoELoRALayer:
         self.route_ws = _bytes(route_workspace_bytes(dims), device)
         self.saved = _bytes(forward_saved_bytes(dims), device)
         self.ws = _bytes(workspace_bytes(dims), device)
-        self.y = torch.empty(dims.T, dims.d, dtype=torch.bfloat16, device=device)
+        self.y = torch.empty(dims.T, dims.d, dtype=dims.elem, device=device)
         self.grads = empty_grads(dims, device)
         self.router_grads: Optional[RouterGrads] = None
 

@@ -17,7 +17,10 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 OBJ = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libmoe_lora.so")
-SOURCES = ("api.hip", "route.hip", "gemm.hip", "stream.hip", "prepass.hip", "grads.hip", "layer.hip", "tune.hip", "timing.hip")
+SOURCES = ("api.hip", "route.hip", "gemm.hip", "stream.hip", "prepass.hip", "grads.hip", "combine.hip",
+           "layer.hip", "tune.hip", "timing.hip")
+# compiled a second time with fp16 elements (-DMOE_F16, objects *_f16.o)
+ELEMENT_SOURCES = ("gemm.hip", "stream.hip", "prepass.hip", "grads.hip", "combine.hip")
 ARCH = "gfx950"
 
 HIPCC_FLAGS = [
@@ -38,8 +41,8 @@ def _hipcc() -> str:
     raise RuntimeError("hipcc not found; the MoE-LoRA library needs ROCm's hipcc")
 
 
-def _compile(src: str, extra: list[str]) -> str:
-    obj = os.path.join(OBJ, os.path.splitext(src)[0] + ".o")
+def _compile(src: str, extra: list[str], suffix: str = "") -> str:
+    obj = os.path.join(OBJ, os.path.splitext(src)[0] + suffix + ".o")
     cmd = [_hipcc(), *HIPCC_FLAGS, *extra, "-c", os.path.join(CSRC, src), "-o", obj]
     res = subprocess.run(cmd, capture_output=True, text=True)
     if res.returncode != 0:
@@ -57,8 +60,9 @@ def build(extra_flags: list[str] | None = None, verbose: bool = True, out: str =
     global OBJ
     OBJ = objdir
     os.makedirs(OBJ, exist_ok=True)
-    with cf.ThreadPoolExecutor(max_workers=len(SOURCES)) as ex:
-        objs = list(ex.map(lambda s: _compile(s, extra), SOURCES))
+    jobs = [(s, extra, "") for s in SOURCES] + [(s, extra + ["-DMOE_F16"], "_f16") for s in ELEMENT_SOURCES]
+    with cf.ThreadPoolExecutor(max_workers=min(len(jobs), 16)) as ex:
+        objs = list(ex.map(lambda j: _compile(*j), jobs))
     tmp = out + ".tmp"
     cmd = [_hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs, "-o", tmp]
     res = subprocess.run(cmd, capture_output=True, text=True)

@@ -17,6 +17,7 @@ moe_status check_dims(const moe_dims* dm) {
   if (dm->k < 1 || dm->k > dm->E) return MOE_ERROR_INVALID_VALUE;
   if (dm->n_shared != 0 && dm->n_shared != 1) return MOE_ERROR_INVALID_VALUE;
   if (!isfinite(dm->lora_scale)) return MOE_ERROR_INVALID_VALUE;
+  if (dm->dtype != MOE_BF16 && dm->dtype != MOE_F16) return MOE_ERROR_INVALID_VALUE;
   if (dm->d % 64 || dm->n % 64 || dm->E > 256 || dm->r > 128) return MOE_ERROR_UNSUPPORTED;
   const int64_t ptot = dm->T * (int64_t)dm->k + (int64_t)dm->n_shared * dm->T;
   if (ptot >= ((int64_t)1 << 31)) return MOE_ERROR_UNSUPPORTED;
@@ -43,7 +44,8 @@ Layer make_layer(const moe_dims* dm) {
   L.Ptot = L.P + L.S * L.T;
   L.s = dm->lora_scale;
   L.ncu = device_cu_count();
-  L.engines = lookup_engines(dm->d, dm->n, dm->E, dm->k, dm->r, dm->n_shared);
+  L.f16 = dm->dtype == MOE_F16;
+  L.engines = lookup_engines(dm->d, dm->n, dm->E, dm->k, dm->r, dm->n_shared, L.f16);
   return L;
 }
 
@@ -64,6 +66,9 @@ moe_status check_weights(const moe_weights* w) {
 }
 
 moe_status launched(hipError_t e) { return e == hipSuccess ? MOE_SUCCESS : MOE_ERROR_LAUNCH; }
+
+// The element-type-dependent launchers of the layer's type.
+#define EL(L, fn, ...) ((L).f16 ? ::moe::el_f16::fn(__VA_ARGS__) : ::moe::el_bf16::fn(__VA_ARGS__))
 
 void attach_common(Layer& L, const moe_routing* rt, const moe_weights* w, const moe_dims* dm,
                    void* ws) {
@@ -177,9 +182,9 @@ moe_status moe_lora_forward(const moe_dims* dm, const moe_bf16* x, const moe_rou
   L.y = y;
   hipError_t e = maybe_pack(L, w, s);
   if (e == hipSuccess) e = launch_gather_table(L, (int32_t*)L.tok, (float*)L.wgt, s);
-  if (e == hipSuccess) e = gemm_gate_up(L, s);
-  if (e == hipSuccess) e = gemm_down(L, s);
-  if (e == hipSuccess) e = launch_combine(L, true, L.o, L.y, s);
+  if (e == hipSuccess) e = EL(L, gemm_gate_up, L, s);
+  if (e == hipSuccess) e = EL(L, gemm_down, L, s);
+  if (e == hipSuccess) e = EL(L, launch_combine, L, true, L.o, L.y, s);
   return launched(e);
 }
 
@@ -220,11 +225,11 @@ moe_status moe_lora_backward(const moe_dims* dm, const moe_bf16* dy, const moe_b
                                                dm->n_shared).dw_part);
   }
   hipError_t e = maybe_pack(L, w, s);
-  if (e == hipSuccess) e = gemm_dh(L, s);
+  if (e == hipSuccess) e = EL(L, gemm_dh, L, s);
   if (e == hipSuccess && router) e = launch_router_grad(L, d_topk_w, d_logits, s);
-  if (e == hipSuccess) e = gemm_dx(L, s);
-  if (e == hipSuccess) e = launch_combine(L, false, L.o, L.dx, s);
-  if (e == hipSuccess) e = gemm_lora_grads(L, s);
+  if (e == hipSuccess) e = EL(L, gemm_dx, L, s);
+  if (e == hipSuccess) e = EL(L, launch_combine, L, false, L.o, L.dx, s);
+  if (e == hipSuccess) e = EL(L, gemm_lora_grads, L, s);
   return launched(e);
 }
 

@@ -39,6 +39,7 @@
 #include "kernels.h"
 
 namespace moe {
+inline namespace MOE_EL {
 
 #ifndef MOE_PGR
 #define MOE_PGR 2
@@ -1113,7 +1114,7 @@ static int mtiles_bound(const Layer& L, int BM) { return L.Ptot / BM + L.Et; }
 template <int KIND>
 static void launch_prepass(const Layer& L, hipStream_t st, const char* name) {
   if ((L.engines & ENG_RANK_STREAM) && L.rs <= 64) {
-    stream_prepass(L, KIND, st);
+    (void)stream_prepass(L, KIND, st);
     return;
   }
   const int mt = mtiles_bound(L, 128);
@@ -1238,4 +1239,5 @@ hipError_t gemm_lora_grads(const Layer& L, hipStream_t st) {
   return hipGetLastError();
 }
 
+}  // inline namespace MOE_EL
 }  // namespace moe

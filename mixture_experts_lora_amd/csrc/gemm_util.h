@@ -6,6 +6,7 @@
 #include "kernels.h"
 
 namespace moe {
+inline namespace MOE_EL {
 
 constexpr int MAX_ET = 512;  // experts (routed + shared) a schedule prefix can hold
 
@@ -173,4 +174,5 @@ __device__ __forceinline__ int gu_row(int n, int j0, int c) {
   return ((grp & 1) ? n : 0) + j0 + (grp >> 1) * 32 + (c & 31);
 }
 
+}  // inline namespace MOE_EL
 }  // namespace moe

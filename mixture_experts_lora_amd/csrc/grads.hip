@@ -25,6 +25,7 @@
 #include "kernels.h"
 
 namespace moe {
+inline namespace MOE_EL {
 namespace {
 
 constexpr int GK = 32;               // segment rows per ring stage
@@ -300,4 +301,5 @@ hipError_t dma_lora_grads(const Layer& L, hipStream_t st) {
   return hipGetLastError();
 }
 
+}  // inline namespace MOE_EL
 }  // namespace moe

@@ -5,6 +5,14 @@
 #include <stddef.h>
 #include <stdint.h>
 
+#ifndef MOE_EL
+#ifdef MOE_F16
+#define MOE_EL el_f16
+#else
+#define MOE_EL el_bf16
+#endif
+#endif
+
 namespace moe {
 
 typedef uint16_t bf16_t;
@@ -26,6 +34,7 @@ enum EngineBits : uint32_t {
 
 struct Layer {
   int T, d, n, E, k, r, S, Et;
+  int f16;           // elements are fp16 (else bf16)
   uint32_t engines;  // EngineBits
   int rs;       // row stride of the rank-r activations (r rounded up to 8)
   int ra;       // row stride used to read A_gu / A_dn (r, or rs for the packed copies)
@@ -96,41 +105,58 @@ hipError_t launch_route(const float* logits, int64_t T, int E, int k, int32_t* i
                         int32_t* counts, int32_t* offsets, int32_t* sorted_pair,
                         int32_t* pair_pos, void* ws, hipStream_t st);
 
-// Grouped GEMM launchers (gemm.hip).
-// Streamed main GEMMs (stream.hip): the product only, without the pre-pass.
-// Rank-r pre-passes (s X A_gu, s H A_dn, s dY B_dn^T, s dG B_gu^T) on the
-// streamed path, for rs <= 64 (prepass.hip).
+// Rank-r pre-pass kinds: s X A_gu, s H A_dn, s dY B_dn^T, s dG B_gu^T.
 enum PrepassKind { PRE_XA = 0, PRE_HA = 1, PRE_QDN = 2, PRE_QGU = 3 };
-hipError_t stream_prepass(const Layer& L, int kind, hipStream_t st);
-hipError_t stream_gate_up(const Layer& L, hipStream_t st);
-hipError_t stream_down(const Layer& L, hipStream_t st);
-hipError_t stream_dx(const Layer& L, hipStream_t st);
-hipError_t stream_dh(const Layer& L, hipStream_t st);
-hipError_t gemm_gate_up(const Layer& L, hipStream_t st);   // G, H  (+ X A_gu pre-pass)
-hipError_t gemm_down(const Layer& L, hipStream_t st);      // O     (+ H A_dn pre-pass)
-hipError_t gemm_dh(const Layer& L, hipStream_t st);        // dG    (+ dO B_dn^T pre-pass)
-hipError_t gemm_dx(const Layer& L, hipStream_t st);        // dX per pair (+ dG B_gu^T)
-hipError_t gemm_lora_grads(const Layer& L, hipStream_t st);  // dA, dB of both modules
-// LDS-DMA LoRA gradients (grads.hip), rank <= 64, before the split-K reduce.
-hipError_t dma_lora_grads(const Layer& L, hipStream_t st);
 
-// Element-wise / gather kernels (layer.hip).
+// Launchers that depend on the element type, declared for both builds (the
+// sources are compiled once with bf16 and once with fp16 elements, into
+// moe::el_bf16 and moe::el_f16; code of one build calls its own unqualified).
+#define MOE_ELEMENT_LAUNCHERS                                                                     \
+  /* grouped GEMMs with their rank-r pre-pass (gemm.hip) */                                       \
+  hipError_t gemm_gate_up(const Layer& L, hipStream_t st);    /* G, H (+ X A_gu) */                \
+  hipError_t gemm_down(const Layer& L, hipStream_t st);       /* O (+ H A_dn) */                   \
+  hipError_t gemm_dh(const Layer& L, hipStream_t st);         /* dG (+ dO B_dn^T) */               \
+  hipError_t gemm_dx(const Layer& L, hipStream_t st);         /* dX per pair (+ dG B_gu^T) */      \
+  hipError_t gemm_lora_grads(const Layer& L, hipStream_t st); /* dA, dB of both modules */         \
+  uint32_t default_engines(); /* the engines used when none was chosen for a shape */             \
+  /* whether the Q_dn pre-pass also writes w Q_dn and w (s H A_dn) (the streamed one does) */     \
+  bool prepass_writes_weighted_rows(const Layer& L);                                              \
+  /* streamed products without their pre-pass (stream.hip) */                                     \
+  hipError_t stream_gate_up(const Layer& L, hipStream_t st);                                      \
+  hipError_t stream_down(const Layer& L, hipStream_t st);                                         \
+  hipError_t stream_dx(const Layer& L, hipStream_t st);                                           \
+  hipError_t stream_dh(const Layer& L, hipStream_t st);                                           \
+  /* streamed rank-r pre-passes, rs <= 64 (prepass.hip) */                                        \
+  hipError_t stream_prepass(const Layer& L, int kind, hipStream_t st);                            \
+  /* LDS-DMA LoRA gradients, rank <= 64 (grads.hip) */                                            \
+  hipError_t dma_lora_grads(const Layer& L, hipStream_t st);                                      \
+  /* weighted gather-combine of per-pair rows into token rows (combine.hip) */                   \
+  hipError_t launch_combine(const Layer& L, bool weighted, const bf16_t* src, bf16_t* dst,        \
+                            hipStream_t st);
+
+inline namespace MOE_EL {
+MOE_ELEMENT_LAUNCHERS
+}
+#ifdef MOE_F16
+namespace el_bf16 {
+MOE_ELEMENT_LAUNCHERS
+}
+#else
+namespace el_f16 {
+MOE_ELEMENT_LAUNCHERS
+}
+#endif
+
+// Element-wise / gather kernels that do not depend on the element type
+// (layer.hip).
 hipError_t launch_pack_a(const Layer& L, const bf16_t* a_gu_src, const bf16_t* a_dn_src,
                          bf16_t* a_gu_dst, bf16_t* a_dn_dst, hipStream_t st);
 hipError_t launch_gather_table(const Layer& L, int32_t* tok, float* wgt, hipStream_t st);
 // Routing-weight and logit gradients from the dh epilogue's partials.
 hipError_t launch_router_grad(const Layer& L, float* d_topk_w, float* d_logits, hipStream_t st);
-// Whether gemm_dh writes the <dH, H> partials (the streamed dh does).
-// The engines this build uses when nothing else was chosen for a shape.
-uint32_t default_engines();
-// Whether the Q_dn pre-pass also writes w Q_dn and w (s H A_dn) (the streamed
-// pre-pass does); otherwise the LoRA gradients compute them first.
-bool prepass_writes_weighted_rows(const Layer& L);
-// Shape -> engines table (api.hip): a recorded choice, else default_engines().
-uint32_t lookup_engines(int d, int n, int E, int k, int r, int S);
-void record_engines(int d, int n, int E, int k, int r, int S, uint32_t engines);
-hipError_t launch_combine(const Layer& L, bool weighted, const bf16_t* src, bf16_t* dst,
-                          hipStream_t st);
+// Shape -> engines table (tune.hip): a recorded choice, else default_engines().
+uint32_t lookup_engines(int d, int n, int E, int k, int r, int S, int f16);
+void record_engines(int d, int n, int E, int k, int r, int S, int f16, uint32_t engines);
 
 int device_cu_count();
 

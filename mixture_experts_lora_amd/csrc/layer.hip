@@ -1,4 +1,5 @@
-// Gather-combine, LoRA-factor packing and buffer layouts.
+// Gather table, LoRA-factor packing, router gradients and buffer layouts
+// (nothing here depends on the element type).
 #include <atomic>
 
 #include <algorithm>
@@ -117,45 +118,6 @@ hipError_t launch_gather_table(const Layer& L, int32_t* tok, float* wgt, hipStre
   return hipGetLastError();
 }
 
-// dst[t] = sum_j w[t,j] * src[pair_pos[t*k+j]]  (+ src[P + t] for the shared
-// expert), fp32 sum in slot order; w = 1 when not weighted (the backward,
-// where the routing weight already entered through dO).
-__global__ __launch_bounds__(256) void k_combine(const Layer L, int weighted,
-                                                 const bf16_t* __restrict__ src,
-                                                 bf16_t* __restrict__ dst) {
-  const int t = blockIdx.x;
-  const int d = L.d, k = L.k;
-  for (int c = threadIdx.x * 8; c < d; c += 256 * 8) {
-    float acc[8];
-#pragma unroll
-    for (int q = 0; q < 8; ++q) acc[q] = 0.0f;
-    for (int j = 0; j < k; ++j) {
-      const int64_t i = (int64_t)t * k + j;
-      const int64_t p = L.pair_pos[i];
-      const float w = weighted ? L.topk_w[i] : 1.0f;
-      const uint4 v = *(const uint4*)(src + p * d + c);
-      const uint32_t u[4] = {v.x, v.y, v.z, v.w};
-#pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        acc[2 * q] += w * bf2f((bf16_t)(u[q] & 0xffffu));
-        acc[2 * q + 1] += w * bf2f((bf16_t)(u[q] >> 16));
-      }
-    }
-    if (L.S) {
-      const uint4 v = *(const uint4*)(src + ((int64_t)L.P + t) * d + c);
-      const uint32_t u[4] = {v.x, v.y, v.z, v.w};
-#pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        acc[2 * q] += bf2f((bf16_t)(u[q] & 0xffffu));
-        acc[2 * q + 1] += bf2f((bf16_t)(u[q] >> 16));
-      }
-    }
-    *(uint4*)(dst + (int64_t)t * d + c) =
-        make_uint4(pack2(acc[0], acc[1]), pack2(acc[2], acc[3]), pack2(acc[4], acc[5]),
-                   pack2(acc[6], acc[7]));
-  }
-}
-
 // Gradients that reach the router (for a model that trains it; the layer's
 // own backward leaves the router frozen, "Faster LoRA MoE training").  Y[t]
 // is linear in the routing weights, so d w[t, j] = <dY[t], O(t, j)>, which
@@ -195,12 +157,6 @@ __global__ __launch_bounds__(64) void k_router_grad(const Layer L, float* __rest
 
 hipError_t launch_router_grad(const Layer& L, float* d_topk_w, float* d_logits, hipStream_t st) {
   MOE_LAUNCH("router_grad", k_router_grad, dim3(L.T), dim3(64), 0, st, L, d_topk_w, d_logits);
-  return hipGetLastError();
-}
-
-hipError_t launch_combine(const Layer& L, bool weighted, const bf16_t* src, bf16_t* dst,
-                          hipStream_t st) {
-  MOE_LAUNCH(weighted ? "combine_y" : "combine_dx", k_combine, dim3(L.T), dim3(256), 0, st, L, weighted ? 1 : 0, src, dst);
   return hipGetLastError();
 }
 

@@ -25,6 +25,7 @@
 #include "kernels.h"
 
 namespace moe {
+inline namespace MOE_EL {
 namespace {
 
 constexpr int QB = 160;                    // rows of a block at most
@@ -42,8 +43,8 @@ typedef short v4s __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) v4s lds_v4s;
 typedef unsigned v2u __attribute__((ext_vector_type(2)));
 
-__device__ __forceinline__ float s_lo(uint32_t w) { return __uint_as_float(w << 16); }
-__device__ __forceinline__ float s_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+__device__ __forceinline__ float s_lo(uint32_t w) { return bf2f((bf16_t)(w & 0xffffu)); }
+__device__ __forceinline__ float s_hi(uint32_t w) { return bf2f((bf16_t)(w >> 16)); }
 
 template <int KIND>
 struct QP {
@@ -249,4 +250,5 @@ hipError_t stream_prepass(const Layer& L, int kind, hipStream_t st) {
   }
 }
 
+}  // inline namespace MOE_EL
 }  // namespace moe

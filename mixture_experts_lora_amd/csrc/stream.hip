@@ -39,6 +39,7 @@
 #include "kernels.h"
 
 namespace moe {
+inline namespace MOE_EL {
 namespace {
 
 constexpr int SBM = 256, SBN = 256;             // tile
@@ -343,8 +344,8 @@ __device__ __forceinline__ void s_store(rsrc_t r, uint32_t voff, uint4 v) {
   const v4u a = {v.x, v.y, v.z, v.w};
   __builtin_amdgcn_raw_buffer_store_b128(a, r, voff, 0, 0);
 }
-__device__ __forceinline__ float s_lo(uint32_t w) { return __uint_as_float(w << 16); }
-__device__ __forceinline__ float s_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+__device__ __forceinline__ float s_lo(uint32_t w) { return bf2f((bf16_t)(w & 0xffffu)); }
+__device__ __forceinline__ float s_hi(uint32_t w) { return bf2f((bf16_t)(w >> 16)); }
 
 // dh epilogue: dH (without the routing weight) of fragment pair (fm, pr) is
 // staged as above and read back by rows: lane -> row (lane / 8) + 8 i,
@@ -627,4 +628,5 @@ hipError_t stream_down(const Layer& L, hipStream_t st) { return launch_stream<SK
 hipError_t stream_dx(const Layer& L, hipStream_t st) { return launch_stream<SK_DX>(L, st, "dx"); }
 hipError_t stream_dh(const Layer& L, hipStream_t st) { return launch_stream<SK_DH>(L, st, "dh"); }
 
+}  // inline namespace MOE_EL
 }  // namespace moe

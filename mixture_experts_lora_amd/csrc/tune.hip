@@ -16,18 +16,18 @@ namespace moe {
 
 namespace {
 std::mutex g_mu;
-std::map<std::array<int, 6>, uint32_t> g_table;
+std::map<std::array<int, 7>, uint32_t> g_table;
 }  // namespace
 
-uint32_t lookup_engines(int d, int n, int E, int k, int r, int S) {
+uint32_t lookup_engines(int d, int n, int E, int k, int r, int S, int f16) {
   std::lock_guard<std::mutex> lock(g_mu);
-  const auto it = g_table.find({d, n, E, k, r, S});
+  const auto it = g_table.find({d, n, E, k, r, S, f16});
   return it == g_table.end() ? default_engines() : it->second;
 }
 
-void record_engines(int d, int n, int E, int k, int r, int S, uint32_t engines) {
+void record_engines(int d, int n, int E, int k, int r, int S, int f16, uint32_t engines) {
   std::lock_guard<std::mutex> lock(g_mu);
-  g_table[{d, n, E, k, r, S}] = engines;
+  g_table[{d, n, E, k, r, S, f16}] = engines;
 }
 
 }  // namespace moe
@@ -132,13 +132,13 @@ extern "C" {
 
 moe_status moe_set_engines(const moe_dims* dm, unsigned engines) {
   if (!dm || (engines & ~(unsigned)ENG_ALL)) return MOE_ERROR_INVALID_VALUE;
-  record_engines(dm->d, dm->n, dm->E, dm->k, dm->r, dm->n_shared, engines);
+  record_engines(dm->d, dm->n, dm->E, dm->k, dm->r, dm->n_shared, dm->dtype == MOE_F16, engines);
   return MOE_SUCCESS;
 }
 
 unsigned moe_get_engines(const moe_dims* dm) {
   if (!dm) return default_engines();
-  return lookup_engines(dm->d, dm->n, dm->E, dm->k, dm->r, dm->n_shared);
+  return lookup_engines(dm->d, dm->n, dm->E, dm->k, dm->r, dm->n_shared, dm->dtype == MOE_F16);
 }
 
 size_t moe_autotune_scratch_bytes(const moe_dims* dm) {

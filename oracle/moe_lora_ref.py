@@ -51,8 +51,9 @@ tests):
     for a model whose router is trained (the selection is taken as locally
     constant, the shared expert's weight as the constant 1).
 
-Arithmetic: float64 by default (float32 on request, used for timing); bf16
-inputs are decoded exactly; no intermediate rounding.
+Arithmetic: float64 by default (float32 on request, used for timing); the
+16-bit inputs (bf16, or IEEE fp16 for a layer whose element type is "f16")
+are decoded exactly; no intermediate rounding.
 """
 from __future__ import annotations
 
@@ -63,6 +64,8 @@ import numpy as np
 __all__ = [
     "Routing",
     "bf16_decode",
+    "f16_decode",
+    "decode",
     "topk_softmax",
     "route",
     "route_naive",
@@ -90,6 +93,36 @@ def bf16_decode(bits: np.ndarray, dtype=np.float64) -> np.ndarray:
         return a.astype(dtype, copy=False)
     u = a.astype(np.uint32) << np.uint32(16)
     return u.view(np.float32).astype(dtype, copy=False)
+
+
+def f16_decode(bits: np.ndarray, dtype=np.float64) -> np.ndarray:
+    """IEEE 754 binary16 bit patterns (uint16) -> exact float values.
+
+    Written from the format's definition: sign bit, 5-bit exponent with bias
+    15, 10-bit fraction; exponent 0 holds the subnormals (fraction * 2^-24),
+    exponent 31 infinities and NaNs.  Floating-point arrays are only cast."""
+    a = np.asarray(bits)
+    if a.dtype != np.uint16:
+        return a.astype(dtype, copy=False)
+    u = a.astype(np.int64)
+    sign = np.where(u >> 15, -1.0, 1.0)
+    ex = (u >> 10) & 0x1F
+    fr = (u & 0x3FF).astype(np.float64)
+    normal = np.ldexp(1.0 + fr / 1024.0, ex - 15)
+    sub = np.ldexp(fr, -24)
+    special = np.where(fr == 0, np.inf, np.nan)
+    v = np.where(ex == 0, sub, np.where(ex == 31, special, normal))
+    return (sign * v).astype(dtype, copy=False)
+
+
+_DECODERS = {"bf16": bf16_decode, "f16": f16_decode}
+
+
+def decode(inp, name: str, dtype=np.float64) -> np.ndarray:
+    """Exact values of the 16-bit input array ``name`` of ``inp``, read in the
+    layer's element type (``inp.dims.element``; bf16 when absent)."""
+    element = getattr(inp.dims, "element", "bf16")
+    return _DECODERS[element](getattr(inp, name), dtype)
 
 
 # ----------------------------------------------------------------------------
@@ -176,7 +209,7 @@ def silu(x: np.ndarray) -> np.ndarray:
 
 
 def _params(inp, dtype):
-    return {name: bf16_decode(getattr(inp, name), dtype)
+    return {name: decode(inp, name, dtype)
             for name in ("w_gu", "w_dn", "a_gu", "b_gu", "a_dn", "b_dn")}
 
 
@@ -210,7 +243,7 @@ def forward(inp, topk_ids, topk_w, dims, dtype=np.float64, keep=False):
     T, d, n, k, E = dims.T, dims.d, dims.n, dims.k, dims.E
     s = dims.lora_scale
     W = _params(inp, dtype)
-    X = bf16_decode(inp.x, dtype)
+    X = decode(inp, "x", dtype)
     R = route(topk_ids, E)
     P = T * k
     P_tot = dims.P_tot
@@ -251,7 +284,7 @@ def forward_naive(inp, topk_ids, topk_w, dims, dtype=np.float64):
     T, d, n, E = dims.T, dims.d, dims.n, dims.E
     s = dims.lora_scale
     W = _params(inp, dtype)
-    X = bf16_decode(inp.x, dtype)
+    X = decode(inp, "x", dtype)
     w = np.asarray(topk_w, dtype=np.float32).astype(dtype)
     y = np.zeros((T, d), dtype)
     for e, (tok, slot) in enumerate(route_naive(topk_ids, E)):
@@ -270,7 +303,7 @@ def forward_merged(inp, topk_ids, topk_w, dims, dtype=np.float64):
     T, d, n, E = dims.T, dims.d, dims.n, dims.E
     s = dims.lora_scale
     W = _params(inp, dtype)
-    X = bf16_decode(inp.x, dtype)
+    X = decode(inp, "x", dtype)
     w = np.asarray(topk_w, dtype=np.float32).astype(dtype)
     y = np.zeros((T, d), dtype)
     for e, (tok, slot) in enumerate(route_naive(topk_ids, dims.E_tot)):
@@ -292,7 +325,7 @@ def forward_tokens(inp, topk_ids, topk_w, dims, tokens, dtype=np.float64):
     """Y rows for the listed tokens only (each from its own k pairs)."""
     n, k, s = dims.n, dims.k, dims.lora_scale
     W = _params(inp, dtype)
-    X = bf16_decode(inp.x, dtype)
+    X = decode(inp, "x", dtype)
     w = np.asarray(topk_w, dtype=np.float32).astype(dtype)
     ids = np.asarray(topk_ids)
     out = np.zeros((len(tokens), dims.d), dtype)
@@ -347,8 +380,8 @@ def backward(inp, topk_ids, topk_w, dims, dtype=np.float64):
     T, d, n, r, k, E = dims.T, dims.d, dims.n, dims.r, dims.k, dims.E
     s = dims.lora_scale
     W = _params(inp, dtype)
-    X = bf16_decode(inp.x, dtype)
-    dY = bf16_decode(inp.dy, dtype)
+    X = decode(inp, "x", dtype)
+    dY = decode(inp, "dy", dtype)
     w = np.asarray(topk_w, dtype=np.float32).astype(dtype).reshape(-1)
     R = route(topk_ids, E)
     P = T * k
@@ -385,8 +418,8 @@ def backward_tokens(inp, topk_ids, topk_w, dims, tokens, dtype=np.float64):
     """dX rows for the listed tokens only."""
     n, k, s = dims.n, dims.k, dims.lora_scale
     W = _params(inp, dtype)
-    X = bf16_decode(inp.x, dtype)
-    dY = bf16_decode(inp.dy, dtype)
+    X = decode(inp, "x", dtype)
+    dY = decode(inp, "dy", dtype)
     w = np.asarray(topk_w, dtype=np.float32).astype(dtype)
     ids = np.asarray(topk_ids)
     out = np.zeros((len(tokens), dims.d), dtype)
@@ -403,8 +436,8 @@ def lora_grads_expert(inp, topk_ids, topk_w, dims, e, dtype=np.float64):
     """(dA_gu, dB_gu, dA_dn, dB_dn) of one expert, from all of its rows."""
     T, k, n, s = dims.T, dims.k, dims.n, dims.lora_scale
     W = _params(inp, dtype)
-    X = bf16_decode(inp.x, dtype)
-    dY = bf16_decode(inp.dy, dtype)
+    X = decode(inp, "x", dtype)
+    dY = decode(inp, "dy", dtype)
     w = np.asarray(topk_w, dtype=np.float32).astype(dtype)
     if e < dims.E:
         tok, slot = np.nonzero(np.asarray(topk_ids) == e)
@@ -434,7 +467,7 @@ def router_grads(inp, topk_ids, topk_w, dims, dtype=np.float64):
     """
     T, k = dims.T, dims.k
     fw = forward(inp, topk_ids, topk_w, dims, dtype)
-    dY = bf16_decode(inp.dy, dtype)
+    dY = decode(inp, "dy", dtype)
     o = fw["o_pair"][:T * k].reshape(T, k, dims.d)
     dw = (dY[:, None, :] * o).sum(axis=2)
     return _softmax_topk_backward(dw, topk_ids, topk_w, dims.E, dtype)
@@ -453,8 +486,8 @@ def router_grads_tokens(inp, topk_ids, topk_w, dims, tokens, dtype=np.float64):
     pairs, as ``forward_tokens``)."""
     n, k, s = dims.n, dims.k, dims.lora_scale
     W = _params(inp, dtype)
-    X = bf16_decode(inp.x, dtype)
-    dY = bf16_decode(inp.dy, dtype)
+    X = decode(inp, "x", dtype)
+    dY = decode(inp, "dy", dtype)
     ids = np.asarray(topk_ids)
     dw = np.zeros((len(tokens), k), dtype)
     for i, t in enumerate(tokens):

@@ -13,7 +13,9 @@ Recipe (fixed; both sides of every parity test consume exactly these arrays):
   ``SeedSequence(seed)`` in the fixed order logits, bias/popularity, x, w_gu,
   w_dn, a_gu, b_gu, a_dn, b_dn, dy.
 * Normal draws are made in fp32 (``standard_normal(dtype=float32)``), scaled by
-  the standard deviation in fp32 and stored as bf16 with round-to-nearest-even.
+  the standard deviation in fp32 and stored as bf16 with round-to-nearest-even
+  (as IEEE fp16, also round-to-nearest-even, for a layer whose element type is
+  ``"f16"``; the draws are the same).
 * Router logits stay fp32.  Recipes:
   ``normal``  N(0,1)  (near-uniform expert load);
   ``bias``    N(0,1) + b_e with b_e ~ N(0, 0.5) per expert;
@@ -42,6 +44,8 @@ class LayerDims:
     T tokens, hidden size d, expert intermediate size n, E routed experts,
     top-k, LoRA rank r, n_shared always-on shared experts (0 or 1) stacked
     after the routed ones, and the LoRA scale applied to the low-rank term.
+    ``element`` is the 16-bit storage type of the activations and weights:
+    ``"bf16"`` or ``"f16"``.
     """
 
     T: int
@@ -54,6 +58,7 @@ class LayerDims:
     lora_scale: float = 1.0
     logits_recipe: str = "normal"
     name: str = field(default="custom", compare=False)
+    element: str = "bf16"
 
     @property
     def P(self) -> int:
@@ -93,16 +98,25 @@ def bf16_bits_from_f32(a: np.ndarray) -> np.ndarray:
     return ((u + bias) >> np.uint32(16)).astype(np.uint16)
 
 
+def f16_bits_from_f32(a: np.ndarray) -> np.ndarray:
+    """Encode fp32 values as IEEE binary16 bit patterns (uint16), round to
+    nearest even (numpy's float32 -> float16 conversion)."""
+    return np.ascontiguousarray(a, dtype=np.float32).astype(np.float16).view(np.uint16)
+
+
+_ENCODE = {"bf16": bf16_bits_from_f32, "f16": f16_bits_from_f32}
+
+
 def _children(seed: int):
     kids = np.random.SeedSequence(seed).spawn(len(_STREAMS))
     return {name: np.random.Generator(np.random.PCG64(s)) for name, s in zip(_STREAMS, kids)}
 
 
-def _normal_bf16(rng: np.random.Generator, shape, std: float) -> np.ndarray:
+def _normal16(rng: np.random.Generator, shape, std: float, element: str) -> np.ndarray:
     v = rng.standard_normal(shape, dtype=np.float32)
     if std != 1.0:
         v *= np.float32(std)
-    return bf16_bits_from_f32(v)
+    return _ENCODE[element](v)
 
 
 def _logits(dims: LayerDims, rng: np.random.Generator, rng_b: np.random.Generator) -> np.ndarray:
@@ -147,7 +161,8 @@ def make_logits(dims: LayerDims, seed: int = 0) -> np.ndarray:
 
 @dataclass
 class LayerInputs:
-    """One layer's inputs; bf16 arrays are uint16 bit patterns.
+    """One layer's inputs; the 16-bit arrays are uint16 bit patterns of
+    ``dims.element`` (bf16 or fp16).
 
     Layouts (row-major): logits [T,E] f32; x, dy [T,d]; w_gu [E_tot,2n,d]
     (rows [0,n) gate, [n,2n) up); w_dn [E_tot,d,n]; a_gu [E_tot,d,r];
@@ -169,15 +184,21 @@ class LayerInputs:
 def make_inputs(dims: LayerDims, seed: int = 0, weight_std: float = 0.02) -> LayerInputs:
     c = _children(seed)
     Et, d, n, r = dims.E_tot, dims.d, dims.n, dims.r
+    if dims.element not in _ENCODE:
+        raise ValueError(f"unknown element type {dims.element!r}")
+
+    def _draw(rng, shape, std):
+        return _normal16(rng, shape, std, dims.element)
+
     return LayerInputs(
         dims=dims,
         logits=_logits(dims, c["logits"], c["bias"]),
-        x=_normal_bf16(c["x"], (dims.T, d), 1.0),
-        w_gu=_normal_bf16(c["w_gu"], (Et, 2 * n, d), weight_std),
-        w_dn=_normal_bf16(c["w_dn"], (Et, d, n), weight_std),
-        a_gu=_normal_bf16(c["a_gu"], (Et, d, r), weight_std),
-        b_gu=_normal_bf16(c["b_gu"], (Et, r, 2 * n), weight_std),
-        a_dn=_normal_bf16(c["a_dn"], (Et, n, r), weight_std),
-        b_dn=_normal_bf16(c["b_dn"], (Et, r, d), weight_std),
-        dy=_normal_bf16(c["dy"], (dims.T, d), 1.0),
+        x=_draw(c["x"], (dims.T, d), 1.0),
+        w_gu=_draw(c["w_gu"], (Et, 2 * n, d), weight_std),
+        w_dn=_draw(c["w_dn"], (Et, d, n), weight_std),
+        a_gu=_draw(c["a_gu"], (Et, d, r), weight_std),
+        b_gu=_draw(c["b_gu"], (Et, r, 2 * n), weight_std),
+        a_dn=_draw(c["a_dn"], (Et, n, r), weight_std),
+        b_dn=_draw(c["b_dn"], (Et, r, d), weight_std),
+        dy=_draw(c["dy"], (dims.T, d), 1.0),
     )

@@ -10,7 +10,7 @@ import torch
 
 import mixture_experts_lora_amd as mel
 
-TOL = 2e-2  # max |gpu - ref| / max |ref| per tensor (bf16 inputs, fp32 accumulate)
+TOL = 2e-2  # max |gpu - ref| / max |ref| per tensor (16-bit inputs, fp32 accumulate)
 
 
 def require_gpu():
@@ -24,12 +24,17 @@ def announce(*parts):
     sys.stdout.flush()
 
 
+ELEMENT = {"bf16": (mel.MOE_BF16, torch.bfloat16), "f16": (mel.MOE_F16, torch.float16)}
+
+
 def mdims(ld) -> mel.Dims:
-    return mel.Dims(ld.T, ld.d, ld.n, ld.E, ld.k, ld.r, ld.n_shared, ld.lora_scale)
+    return mel.Dims(ld.T, ld.d, ld.n, ld.E, ld.k, ld.r, ld.n_shared, ld.lora_scale,
+                    ELEMENT[ld.element][0])
 
 
-def bf16_tensor(bits: np.ndarray, dev="cuda") -> torch.Tensor:
-    return torch.from_numpy(bits.view(np.int16)).to(dev).view(torch.bfloat16)
+def elem_tensor(bits: np.ndarray, dev="cuda", element: str = "bf16") -> torch.Tensor:
+    """uint16 bit patterns of the given element type -> a GPU tensor of it."""
+    return torch.from_numpy(bits.view(np.int16)).to(dev).view(ELEMENT[element][1])
 
 
 def to_numpy_f64(t: torch.Tensor) -> np.ndarray:
@@ -37,10 +42,11 @@ def to_numpy_f64(t: torch.Tensor) -> np.ndarray:
 
 
 def upload(inp, dev="cuda"):
-    w = mel.Weights(*(bf16_tensor(getattr(inp, k), dev) for k in
+    el = inp.dims.element
+    w = mel.Weights(*(elem_tensor(getattr(inp, k), dev, el) for k in
                       ("w_gu", "w_dn", "a_gu", "b_gu", "a_dn", "b_dn")))
     logits = torch.from_numpy(inp.logits).to(dev)
-    return logits, bf16_tensor(inp.x, dev), bf16_tensor(inp.dy, dev), w
+    return logits, elem_tensor(inp.x, dev, el), elem_tensor(inp.dy, dev, el), w
 
 
 def relerr(got, ref) -> float:

@@ -62,7 +62,7 @@ BAD = [
     (dict(k=0), 1), (dict(k=9), 1), (dict(T=0), 1), (dict(r=0), 1), (dict(n_shared=2), 1),
     (dict(lora_scale=float("inf")), 1), (dict(lora_scale=float("nan")), 1),
     (dict(d=96), 2), (dict(n=100), 2), (dict(E=300, k=2), 2), (dict(r=129), 2),
-    (dict(T=1 << 29, k=8), 2),
+    (dict(T=1 << 29, k=8), 2), (dict(dtype=2), 1), (dict(dtype=-1), 1),
 ]
 
 
@@ -122,6 +122,23 @@ def test_python_binding_refuses_cpu_tensors():
     dims = mel.Dims(T=4, d=64, n=64, E=2, k=1, r=4)
     with pytest.raises(ValueError):
         mel.route(torch.zeros(4, 2), dims)
+
+
+def test_dims_struct_layout():
+    # int64 T; six int32; float lora_scale; int32 dtype -> 40 bytes, 8-aligned
+    assert ctypes.sizeof(_lib.MoeDims) == 40 and ctypes.alignment(_lib.MoeDims) == 8
+    assert _lib.MoeDims.lora_scale.offset == 32 and _lib.MoeDims.dtype.offset == 36
+
+
+def test_fp16_dims_accepted_and_keyed_apart(lib):
+    bf, hf = _dims(d=256), _dims(d=256, dtype=_lib.MOE_F16)
+    assert lib.moe_workspace_bytes(ctypes.byref(hf)) == lib.moe_workspace_bytes(ctypes.byref(bf)) > 0
+    before = lib.moe_get_engines(ctypes.byref(bf))
+    other = before ^ 1
+    assert lib.moe_set_engines(ctypes.byref(hf), other) == 0
+    assert lib.moe_get_engines(ctypes.byref(hf)) == other
+    assert lib.moe_get_engines(ctypes.byref(bf)) == before       # the element type is in the key
+    assert lib.moe_set_engines(ctypes.byref(hf), before) == 0
 
 
 def test_engine_table_on_the_host(lib):

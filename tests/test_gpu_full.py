@@ -3,8 +3,10 @@ checked against the oracle on outputs it can compute one by one: Y, dX and
 router-gradient rows of sampled tokens (float64), and the LoRA gradients of
 sampled experts (float32: the least-loaded expert with rows, an empty expert
 when there is one, the most-loaded expert, and the shared expert when there
-is one).
+is one).  The headline shape runs again with fp16 elements.
 Routing at these sizes is compared in full by test_gpu_route."""
+from dataclasses import replace
+
 import numpy as np
 import pytest
 import torch
@@ -16,13 +18,15 @@ from synth import CONFIGS, make_inputs
 
 pytestmark = pytest.mark.gpu
 
-FULL = ["qwen3_30b_a3b", "deepseek_shared", "long_zipf", "routing_stress"]
+FULL = {name: CONFIGS[name] for name in
+        ("qwen3_30b_a3b", "deepseek_shared", "long_zipf", "routing_stress")}
+FULL["qwen3_30b_a3b_f16"] = replace(CONFIGS["qwen3_30b_a3b"], element="f16")
 
 
-@pytest.mark.parametrize("name", FULL)
+@pytest.mark.parametrize("name", list(FULL))
 def test_full_size_sampled(name):
     require_gpu()
-    ld = CONFIGS[name]
+    ld = FULL[name]
     announce("full", name, ld)
     inp = make_inputs(ld, seed=0)
     dims = mdims(ld)

@@ -2,11 +2,14 @@
 element, at sizes the oracle finishes in seconds: several M/N tiles, ragged
 segment tails, ranks that are and are not multiples of 8, a shared expert, a
 LoRA scale other than 1, empty experts, split-K LoRA gradients, k = E, k = 1,
-T = 1; the routing-weight and logit gradients with every case.
+T = 1; the routing-weight and logit gradients with every case; every case
+again with fp16 elements.
 
 Every output buffer is filled with NaN before the call (an unwritten element
 fails), and the whole route + forward + backward runs twice with bitwise equal
 results (no races, no order-dependent sums)."""
+from dataclasses import replace
+
 import numpy as np
 import pytest
 import torch
@@ -31,11 +34,12 @@ CASES = {
     # contraction long enough for the rank-r pre-passes to split over workgroups
     "prepass_splits": LayerDims(200, 1024, 256, 4, 2, 16),
 }
+CASES.update({f"{k}_f16": replace(v, element="f16") for k, v in list(CASES.items())})
 
 
 def _run(dims, logits, x, dy, w):
     rt = mel.route(logits, dims)
-    y = torch.full((dims.T, dims.d), float("nan"), dtype=torch.bfloat16, device="cuda")
+    y = torch.full((dims.T, dims.d), float("nan"), dtype=dims.elem, device="cuda")
     y, saved = mel.forward(x, rt, w, dims, y=y)
     g = mel.empty_grads(dims, "cuda")
     rg = mel.empty_router_grads(dims, "cuda")
@@ -85,12 +89,13 @@ def test_layer_parity(name):
     rt2, y2, g2, rg2 = _run(dims, logits, x, dy, w)
     assert torch.equal(y.view(torch.int16), y2.view(torch.int16))
     for a, b in zip(list(g) + list(rg), list(g2) + list(rg2)):
-        assert torch.equal(a.view(torch.int16) if a.dtype == torch.bfloat16 else a,
-                           b.view(torch.int16) if b.dtype == torch.bfloat16 else b)
+        assert torch.equal(a.view(torch.int16) if a.dtype == dims.elem else a,
+                           b.view(torch.int16) if b.dtype == dims.elem else b)
 
 
 ENGINE_CASES = ["tiny", "ragged_shared_r3_s2", "r128_n192", "empty_experts_r64", "splitk_two_chunks",
-                "wide_d320_zipf"]
+                "wide_d320_zipf", "ragged_shared_r3_s2_f16", "empty_experts_r64_f16",
+                "wide_d320_zipf_f16"]
 
 
 @pytest.mark.parametrize("engines", [0, mel.ENGINE_ALL], ids=["register_path", "streamed"])

@@ -1,9 +1,9 @@
-"""The seeded input generator: reproducible, and its bf16 encoding is
-round-to-nearest-even (checked against torch's own float32 -> bfloat16 cast)."""
+"""The seeded input generator: reproducible, and its bf16 and fp16 encodings
+are round-to-nearest-even (checked against torch's own float32 casts)."""
 import numpy as np
 import torch
 
-from synth import CONFIGS, LayerDims, bf16_bits_from_f32, make_inputs, make_logits
+from synth import CONFIGS, LayerDims, bf16_bits_from_f32, f16_bits_from_f32, make_inputs, make_logits
 
 
 def test_bf16_encoding_matches_torch():
@@ -36,3 +36,20 @@ def test_shapes_and_scales():
     assert abs(float(w.std()) - 0.02) < 0.002
     x = (inp.x.astype(np.uint32) << 16).view(np.float32)
     assert abs(float(x.std()) - 1.0) < 0.05
+
+
+def test_f16_encoding_matches_torch_and_keeps_the_draws():
+    rng = np.random.default_rng(1)
+    v = np.concatenate([rng.standard_normal(100000).astype(np.float32) * 10,
+                        np.array([0.0, -0.0, 1.0, 1 + 2 ** -11, 1 + 3 * 2 ** -11, 2 ** -25,
+                                  3 * 2 ** -26, 65504.0, -6.1e-5], np.float32)])
+    ours = f16_bits_from_f32(v)
+    ref = torch.from_numpy(v).to(torch.float16).view(torch.int16).numpy().view(np.uint16)
+    np.testing.assert_array_equal(ours, ref)
+    # an fp16 layer draws the same normals as its bf16 twin, only stored differently
+    bf = make_inputs(LayerDims(16, 64, 32, 4, 2, 4), seed=3)
+    hf = make_inputs(LayerDims(16, 64, 32, 4, 2, 4, element="f16"), seed=3)
+    xb = (bf.x.astype(np.uint32) << 16).view(np.float32)
+    xh = hf.x.view(np.float16).astype(np.float32)
+    assert np.max(np.abs(xb - xh)) <= 2 ** -8 * np.max(np.abs(xb))
+    np.testing.assert_array_equal(bf.logits, hf.logits)
