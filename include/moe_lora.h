@@ -193,16 +193,16 @@ moe_status moe_lora_backward(const moe_dims* dims, const moe_bf16* dy, const moe
  *   MOE_ENGINE_RANK  the rank-r pre-passes and the LoRA gradients (r <= 64;
  *     above that both settings use the register path).
  * Without a recorded choice a shape uses the build's defaults (everything
- * streamed except gate_up).
+ * streamed).
  * moe_set_engines records a choice (MOE_ERROR_INVALID_VALUE for unknown bits);
  * moe_get_engines returns the choice in force.  Results agree between engines
  * to the layer's tolerance, not bitwise.
  * moe_autotune is the one-time start-up autotune of the faster-MoE page's
  * kernels ("Unsloth MoE Triton kernels"), cached per shape: it runs route +
- * forward + backward on the given inputs once per setting (all streamed, all
- * register-path; one warm-up and three timed steps each, every kernel timed
- * with events), keeps per product the faster engine, records and returns the
- * choice.  Unlike every other entry point it waits for the GPU; it also
+ * forward + backward on the given inputs under each setting (all streamed, all
+ * register-path), twice in alternation (one warm-up and three timed steps
+ * each time, every kernel timed with events), keeps per product the engine
+ * with the lower of its two times, records and returns the choice.  Unlike every other entry point it waits for the GPU; it also
  * switches the kernel-timing recorder off.  scratch: device memory of at
  * least moe_autotune_scratch_bytes(dims), 256-byte aligned, for all the
  * routing, saved, workspace and output buffers of those steps; its contents

@@ -596,11 +596,11 @@ template <> struct MainCfg<24> { using type = Cfg<128, 256, 2, 2, 0, 6, 32>; }; 
 template <> struct MainCfg<25> { using type = Cfg<256, 128, 4, 1, 0, 6, 32>; };     // 4 waves of 64x128, deep ring
 template <> struct MainCfg<26> { using type = Cfg<128, 256, 2, 4, 0, 6, 32>; };     // 8 waves of 64x64, deep ring
 template <> struct MainCfg<27> { using type = Cfg<256, 256, 4, 2, 0, 4, 32>; };     // 8 waves of 64x128
-// Which main products run on the streamed engine (stream.hip): down and dx
-// by default; gate_up is faster on the register-path kernel for now, and dh
-// needs the SwiGLU backward in its epilogue, which only that kernel has.
+// Which main products run on the streamed engine (stream.hip) by default:
+// all four (its 320-row tiles cover a typical expert segment in one tile);
+// the register-path kernels here remain the other engine of each product.
 #ifndef MOE_STREAM_GU
-#define MOE_STREAM_GU 0
+#define MOE_STREAM_GU 1
 #endif
 #ifndef MOE_STREAM_DN
 #define MOE_STREAM_DN 1

@@ -8,19 +8,23 @@
 // added into the same accumulator ("Faster LoRA MoE training").
 //
 // One persistent workgroup per CU runs ONE pipeline over its whole work
-// list: every step moves a 256 x 32 panel of each operand from global memory
-// straight into LDS (buffer_load_dwordx4 ... lds), through a ring of four
-// stages issued three steps ahead.  The step stream runs through a tile's
+// list: every step moves a 32-k panel of each operand (320 rows of A, 256
+// columns of B) from global memory straight into LDS (buffer_load_dwordx4
+// ... lds), through a ring of four stages issued three steps ahead.  The step stream runs through a tile's
 // base K steps, then its rank-r steps, then on into the next tile, so the
 // pipeline never drains between tiles: the next tile's first panels are in
 // flight while the current tile's epilogue writes its outputs.
 //
-//  - tile 256 x 256, 8 waves of 128 x 64, two per SIMD
-//    (v_mfma_f32_32x32x16_bf16, fp32 accumulation, operands swapped so a
-//    lane owns 4 consecutive columns): while one wave of a SIMD waits to
-//    issue a memory instruction (the CU's queues fill with requests that miss
-//    the L2), the other keeps the SIMD's MFMA unit busy;
-//  - row-contiguous panels are stored [256 rows][32 k] with the 16-byte chunk
+//  - tile 320 x 256, 8 waves of 160 x 64, two per SIMD
+//    (v_mfma_f32_32x32x16 on bf16 or fp16, fp32 accumulation, operands
+//    swapped so a lane owns 4 consecutive columns): while one wave of a SIMD
+//    waits to issue a memory instruction (the CU's queues fill with requests
+//    that miss the L2), the other keeps the SIMD's MFMA unit busy;
+//  - 320 rows, not 256: an expert's rows are tiled from its segment start,
+//    and with about 256 +- 16 rows per expert a 256-row tile leaves half the
+//    experts a short tail tile that streams the expert's whole weight panel
+//    again for a few rows; 320 covers such an expert in one tile;
+//  - row-contiguous panels are stored [rows][32 k] with the 16-byte chunk
 //    of row r at position c ^ ((r >> 2) & 3), read with ds_read_b128;
 //  - panels whose contraction index is the row index in memory (W_dn and
 //    W_gu in the backward, B_dn and B_gu in the forward) are stored
@@ -42,18 +46,29 @@ namespace moe {
 inline namespace MOE_EL {
 namespace {
 
-constexpr int SBM = 256, SBN = 256;             // tile
+#ifndef MOE_SBM
+#define MOE_SBM 320
+#endif
+constexpr int SBM = MOE_SBM, SBN = 256;         // tile
 constexpr int SWM = 2, SWN = 4;                 // wave grid
 constexpr int SNW = SWM * SWN, SNT = 64 * SNW;  // 8 waves, two per SIMD
-constexpr int STM = SBM / SWM, STN = SBN / SWN; // 128 x 64 per wave
+constexpr int STM = SBM / SWM, STN = SBN / SWN; // 160 x 64 per wave
 constexpr int SFM = STM / 32, SFN = STN / 32;   // 4 x 2 fragments
 constexpr int SK = 32;                          // k per ring stage
 constexpr int SNS = 4, SPD = SNS - 1;           // ring stages, issue distance
-constexpr int PANEL = SBM * SK;                 // bf16 elements of one operand panel
-constexpr int SSTAGE = 2 * PANEL;               // A panel then B panel
-constexpr int NI = PANEL * 2 / 1024 / SNW;      // DMA instructions per wave per panel
-constexpr int PER = 2 * NI;                     // per wave per stage
-static_assert(NI * SNW * 1024 == PANEL * 2, "panel split");
+constexpr int APAN = SBM * SK, BPAN = SBN * SK;  // 16-bit elements of the A and B panels
+constexpr int SSTAGE = APAN + BPAN;               // A panel then B panel
+// One DMA instruction moves 1 KiB = 16 rows of 32 k.  The B panel splits
+// evenly over the waves; the A panel's AIN instructions go A_FULL to every
+// wave and one more to each of the first A_REM waves.
+constexpr int AIN = SBM / 16, BIN = SBN / 16;
+constexpr int A_FULL = AIN / SNW, A_REM = AIN % SNW;
+constexpr int NIA = A_FULL + (A_REM ? 1 : 0), NIB = BIN / SNW;
+constexpr int PER_HI = NIA + NIB, PER_LO = A_FULL + NIB;  // per wave per stage
+static_assert(SBM % 32 == 0 && BIN % SNW == 0, "panel split");
+static_assert(SNS * SSTAGE * 2 <= 150 * 1024, "ring fits in LDS");
+// gather indices of a tile, in whole 1 KiB DMA instructions (256 tokens)
+constexpr int TOKB = (SBM + 255) / 256 * 256;
 
 enum StreamKind { SK_GU = 0, SK_DN = 1, SK_DH = 2, SK_DX = 3 };
 
@@ -122,7 +137,7 @@ __device__ __forceinline__ int s_prow(int j) {
 // per-lane offsets, and the next step to issue.
 struct SIssue {
   int4v da_m, db_m, da_l, db_l;
-  uint32_t va_m[NI], vb_m[NI], va_l[NI], vb_l[NI];
+  uint32_t va_m[NIA], vb_m[NIB], va_l[NIA], vb_l[NIB];
   uint32_t ldb_bm, ldb_bl;  // byte stride of the MN-panel sources (k rows)
   int step, smain, stot;
 };
@@ -141,7 +156,7 @@ __device__ __forceinline__ void s_setup(const Layer& L, const STile& T, const in
   if constexpr (KIND == SK_GU || KIND == SK_DH) {
     S.da_m = make_desc(KIND == SK_GU ? L.x : L.dy, (int64_t)L.T * d * 2);
 #pragma unroll
-    for (int j = 0; j < NI; ++j) {
+    for (int j = 0; j < NIA; ++j) {
       const int m = s_prow(j);
       S.va_m[j] = m < mrows ? (uint32_t)tok[m] * (uint32_t)(d * 2) + lck * 16 : OOB;
     }
@@ -150,7 +165,7 @@ __device__ __forceinline__ void s_setup(const Layer& L, const STile& T, const in
     const bf16_t* src = KIND == SK_DN ? L.h : L.dg;
     S.da_m = make_desc(src + (int64_t)row0 * lda, (int64_t)mrows * lda * 2);
 #pragma unroll
-    for (int j = 0; j < NI; ++j) {
+    for (int j = 0; j < NIA; ++j) {
       const int m = s_prow(j);
       S.va_m[j] = m < mrows ? (uint32_t)m * (uint32_t)(lda * 2) + lck * 16 : OOB;
     }
@@ -160,7 +175,7 @@ __device__ __forceinline__ void s_setup(const Layer& L, const STile& T, const in
     const bf16_t* src = KIND == SK_GU ? L.xa : KIND == SK_DN ? L.ha : KIND == SK_DH ? L.qdn : L.qgu;
     S.da_l = make_desc(src + (int64_t)row0 * rs, (int64_t)mrows * rs * 2);
 #pragma unroll
-    for (int j = 0; j < NI; ++j) {
+    for (int j = 0; j < NIA; ++j) {
       const int m = s_prow(j);
       S.va_l[j] = m < mrows ? (uint32_t)m * (uint32_t)(rs * 2) + lck * 16 : OOB;
     }
@@ -170,7 +185,7 @@ __device__ __forceinline__ void s_setup(const Layer& L, const STile& T, const in
     const int j0 = T.nt * (SBN / 2);
     S.db_m = make_desc(L.w_gu + (int64_t)e * 2 * n * d, (int64_t)2 * n * d * 2);
 #pragma unroll
-    for (int j = 0; j < NI; ++j) {
+    for (int j = 0; j < NIB; ++j) {
       const int c = s_prow(j);
       const bool ok = j0 + (c >> 6) * 32 + (c & 31) < n;
       S.vb_m[j] = ok ? (uint32_t)gu_row(n, j0, c) * (uint32_t)(d * 2) + lck * 16 : OOB;
@@ -180,13 +195,13 @@ __device__ __forceinline__ void s_setup(const Layer& L, const STile& T, const in
     const int c = lcm * 8;  // tile column of this lane's chunk (8 columns, one gate/up group)
     const bool ok = j0 + (c >> 6) * 32 + (c & 31) < n;
 #pragma unroll
-    for (int j = 0; j < NI; ++j)
+    for (int j = 0; j < NIB; ++j)
       S.vb_l[j] = ok ? (uint32_t)s_krow(j) * S.ldb_bl + (uint32_t)gu_row(n, j0, c) * 2 : OOB;
   } else if constexpr (KIND == SK_DN) {
     const int c0 = T.nt * SBN;
     S.db_m = make_desc(L.w_dn + (int64_t)e * d * n, (int64_t)d * n * 2);
 #pragma unroll
-    for (int j = 0; j < NI; ++j) {
+    for (int j = 0; j < NIB; ++j) {
       const int c = s_prow(j);
       S.vb_m[j] = c0 + c < d ? (uint32_t)(c0 + c) * (uint32_t)(n * 2) + lck * 16 : OOB;
     }
@@ -194,17 +209,17 @@ __device__ __forceinline__ void s_setup(const Layer& L, const STile& T, const in
     S.ldb_bl = d * 2;
     const int col = c0 + lcm * 8;
 #pragma unroll
-    for (int j = 0; j < NI; ++j) S.vb_l[j] = col < d ? (uint32_t)s_krow(j) * S.ldb_bl + (uint32_t)col * 2 : OOB;
+    for (int j = 0; j < NIB; ++j) S.vb_l[j] = col < d ? (uint32_t)s_krow(j) * S.ldb_bl + (uint32_t)col * 2 : OOB;
   } else if constexpr (KIND == SK_DH) {
     const int j0 = T.nt * SBN;
     S.db_m = make_desc(L.w_dn + (int64_t)e * d * n, (int64_t)d * n * 2);
     S.ldb_bm = n * 2;
     const int col = j0 + lcm * 8;
 #pragma unroll
-    for (int j = 0; j < NI; ++j) S.vb_m[j] = col < n ? (uint32_t)s_krow(j) * S.ldb_bm + (uint32_t)col * 2 : OOB;
+    for (int j = 0; j < NIB; ++j) S.vb_m[j] = col < n ? (uint32_t)s_krow(j) * S.ldb_bm + (uint32_t)col * 2 : OOB;
     S.db_l = make_desc(L.a_dn + (int64_t)e * n * ra, (int64_t)n * ra * 2);
 #pragma unroll
-    for (int j = 0; j < NI; ++j) {
+    for (int j = 0; j < NIB; ++j) {
       const int c = s_prow(j);
       S.vb_l[j] = j0 + c < n ? (uint32_t)(j0 + c) * (uint32_t)(ra * 2) + lck * 16 : OOB;
     }
@@ -214,10 +229,10 @@ __device__ __forceinline__ void s_setup(const Layer& L, const STile& T, const in
     S.ldb_bm = d * 2;
     const int col = c0 + lcm * 8;
 #pragma unroll
-    for (int j = 0; j < NI; ++j) S.vb_m[j] = col < d ? (uint32_t)s_krow(j) * S.ldb_bm + (uint32_t)col * 2 : OOB;
+    for (int j = 0; j < NIB; ++j) S.vb_m[j] = col < d ? (uint32_t)s_krow(j) * S.ldb_bm + (uint32_t)col * 2 : OOB;
     S.db_l = make_desc(L.a_gu + (int64_t)e * d * ra, (int64_t)d * ra * 2);
 #pragma unroll
-    for (int j = 0; j < NI; ++j) {
+    for (int j = 0; j < NIB; ++j) {
       const int c = s_prow(j);
       S.vb_l[j] = c0 + c < d ? (uint32_t)(c0 + c) * (uint32_t)(ra * 2) + lck * 16 : OOB;
     }
@@ -228,26 +243,31 @@ __device__ __forceinline__ void s_setup(const Layer& L, const STile& T, const in
 // address `sb` (A panel, then B panel).
 template <int KIND>
 __device__ __forceinline__ void s_issue(const SIssue& S, int step, uint32_t sb, int rs, int r) {
-  const int wid = threadIdx.x >> 6;
-  const uint32_t ma = sb, mb = sb + PANEL * 2;
+  const int wid = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const uint32_t ma = sb, mb = sb + APAN * 2;
+  // A instruction j exists for every wave below A_FULL, for the first A_REM
+  // waves at A_FULL
+  auto a_on = [&](int j) { return j < A_FULL || wid < A_REM; };
   if (step < S.smain) {
     const int k0 = step * SK;
 #pragma unroll
-    for (int j = 0; j < NI; ++j)
-      dma16(S.da_m, S.va_m[j], (uint32_t)k0 * 2u, __builtin_amdgcn_readfirstlane(ma + (wid + j * SNW) * 1024));
+    for (int j = 0; j < NIA; ++j)
+      if (a_on(j))
+        dma16(S.da_m, S.va_m[j], (uint32_t)k0 * 2u, __builtin_amdgcn_readfirstlane(ma + (wid + j * SNW) * 1024));
 #pragma unroll
-    for (int j = 0; j < NI; ++j)
+    for (int j = 0; j < NIB; ++j)
       dma16(S.db_m, S.vb_m[j], SP<KIND>::B_MAIN_MN ? (uint32_t)k0 * S.ldb_bm : (uint32_t)k0 * 2u,
             __builtin_amdgcn_readfirstlane(mb + (wid + j * SNW) * 1024));
   } else {
     const int k0 = (step - S.smain) * SK;
     const int kc = s_lck() * 8;
 #pragma unroll
-    for (int j = 0; j < NI; ++j)
-      dma16(S.da_l, k0 + kc < rs ? S.va_l[j] : OOB, (uint32_t)k0 * 2u,
-            __builtin_amdgcn_readfirstlane(ma + (wid + j * SNW) * 1024));
+    for (int j = 0; j < NIA; ++j)
+      if (a_on(j))
+        dma16(S.da_l, k0 + kc < rs ? S.va_l[j] : OOB, (uint32_t)k0 * 2u,
+              __builtin_amdgcn_readfirstlane(ma + (wid + j * SNW) * 1024));
 #pragma unroll
-    for (int j = 0; j < NI; ++j) {
+    for (int j = 0; j < NIB; ++j) {
       if constexpr (SP<KIND>::B_LORA_MN)
         dma16(S.db_l, k0 + s_krow(j) < r ? S.vb_l[j] : OOB, (uint32_t)k0 * S.ldb_bl,
               __builtin_amdgcn_readfirstlane(mb + (wid + j * SNW) * 1024));
@@ -275,42 +295,50 @@ __device__ __forceinline__ void s_mma(const bf16_t* As, const bf16_t* Bs, f32x16
   // read) at columns 16 (g & 1) + 4 rr of the fragment; the transposing read
   // gives lane (g, j) the 4 k values of column 16 (g & 1) + j.
   const int g = lane >> 4, q = (lane >> 2) & 3, rr = lane & 3;
-  uint4 a[SK / 16][SFM], b[SK / 16][SFN];
+  // fragments of KB k-halves of 16 are held at once: all of the stage's
+  // (KB = 2) or one half's (KB = 1, for tiles whose accumulators leave no
+  // room for both)
+  constexpr int KB = SFM > 4 ? 1 : SK / 16;
 #pragma unroll
-  for (int kk = 0; kk < SK / 16; ++kk) {
-    const int c = ((kk * 2 + (lane >> 5)) ^ swz) * 16;
+  for (int k2 = 0; k2 < SK / 16; k2 += KB) {
+    uint4 a[KB][SFM], b[KB][SFN];
 #pragma unroll
-    for (int fm = 0; fm < SFM; ++fm) a[kk][fm] = *(const uint4*)(ab + fm * 32 * (SK * 2) + c);
-    if constexpr (!BMN) {
-      const char* bb = (const char*)Bs + (wn * STN + l) * (SK * 2);
+    for (int kb = 0; kb < KB; ++kb) {
+      const int kk = k2 + kb;
+      const int c = ((kk * 2 + (lane >> 5)) ^ swz) * 16;
 #pragma unroll
-      for (int fn = 0; fn < SFN; ++fn) b[kk][fn] = *(const uint4*)(bb + fn * 32 * (SK * 2) + c);
-    } else {
-      const int krow = kk * 16 + 8 * (g >> 1) + q;
-      const int kx = (krow & 3) * 4;
+      for (int fm = 0; fm < SFM; ++fm) a[kb][fm] = *(const uint4*)(ab + fm * 32 * (SK * 2) + c);
+      if constexpr (!BMN) {
+        const char* bb = (const char*)Bs + (wn * STN + l) * (SK * 2);
 #pragma unroll
-      for (int fn = 0; fn < SFN; ++fn) {
-        const int col = wn * STN + fn * 32 + 16 * (g & 1) + 4 * rr;
-        const char* p = (const char*)Bs + krow * (SBN * 2) + (((col >> 3) ^ kx) * 16) + (col & 7) * 2;
-        const v4s lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s*)p);
-        const v4s hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s*)(p + 4 * SBN * 2));
-        b[kk][fn] = make_uint4((uint32_t)(uint16_t)lo[0] | ((uint32_t)(uint16_t)lo[1] << 16),
-                               (uint32_t)(uint16_t)lo[2] | ((uint32_t)(uint16_t)lo[3] << 16),
-                               (uint32_t)(uint16_t)hi[0] | ((uint32_t)(uint16_t)hi[1] << 16),
-                               (uint32_t)(uint16_t)hi[2] | ((uint32_t)(uint16_t)hi[3] << 16));
+        for (int fn = 0; fn < SFN; ++fn) b[kb][fn] = *(const uint4*)(bb + fn * 32 * (SK * 2) + c);
+      } else {
+        const int krow = kk * 16 + 8 * (g >> 1) + q;
+        const int kx = (krow & 3) * 4;
+#pragma unroll
+        for (int fn = 0; fn < SFN; ++fn) {
+          const int col = wn * STN + fn * 32 + 16 * (g & 1) + 4 * rr;
+          const char* p = (const char*)Bs + krow * (SBN * 2) + (((col >> 3) ^ kx) * 16) + (col & 7) * 2;
+          const v4s lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s*)p);
+          const v4s hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s*)(p + 4 * SBN * 2));
+          b[kb][fn] = make_uint4((uint32_t)(uint16_t)lo[0] | ((uint32_t)(uint16_t)lo[1] << 16),
+                                 (uint32_t)(uint16_t)lo[2] | ((uint32_t)(uint16_t)lo[3] << 16),
+                                 (uint32_t)(uint16_t)hi[0] | ((uint32_t)(uint16_t)hi[1] << 16),
+                                 (uint32_t)(uint16_t)hi[2] | ((uint32_t)(uint16_t)hi[3] << 16));
+        }
       }
     }
+#pragma unroll
+    for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+      for (int fm = 0; fm < SFM; ++fm)
+#pragma unroll
+        for (int fn = 0; fn < SFN; ++fn) acc[fm][fn] = mfma32(b[kb][fn], a[kb][fm], acc[fm][fn]);
+    // keep that order: the LDS reads of the group, then its MFMAs
+    constexpr int NREAD = KB * (SFM + (BMN ? 2 : 1) * SFN);
+    __builtin_amdgcn_sched_group_barrier(0x100, NREAD, 0);
+    __builtin_amdgcn_sched_group_barrier(0x008, KB * SFM * SFN, 0);
   }
-#pragma unroll
-  for (int kk = 0; kk < SK / 16; ++kk)
-#pragma unroll
-    for (int fm = 0; fm < SFM; ++fm)
-#pragma unroll
-      for (int fn = 0; fn < SFN; ++fn) acc[fm][fn] = mfma32(b[kk][fn], a[kk][fm], acc[fm][fn]);
-  // keep that order: every LDS read of the stage, then the MFMAs
-  constexpr int NREAD = (SK / 16) * (SFM + (BMN ? 2 : 1) * SFN);
-  __builtin_amdgcn_sched_group_barrier(0x100, NREAD, 0);
-  __builtin_amdgcn_sched_group_barrier(0x008, (SK / 16) * SFM * SFN, 0);
 }
 
 // Epilogue, through a private 4 KiB LDS staging area per wave.  The
@@ -387,13 +415,17 @@ __device__ __forceinline__ void s_epilogue_dh(const Layer& L, const STile& T, f3
   // gradient; without a destination every such store falls out of range
   const int G = L.dw_groups;
   const rsrc_t rpart = make_rsrc(L.dw_part, L.dw_part ? P * G * 4 : 0);
+  // with the tall tile's accumulators there is no room to hold a second pair
+  constexpr bool AHEAD = SFM <= 4;
   GUq cur, nxt;
-  s_dh_load(L, T, rg, rw, 0, cur);
+  if (AHEAD) s_dh_load(L, T, rg, rw, 0, cur);
 #pragma unroll
   for (int q = 0; q < SFM * (SFN / 2); ++q) {
     const int fm = q / (SFN / 2), pr = q % (SFN / 2);
-    if (q + 1 < SFM * (SFN / 2)) s_dh_load(L, T, rg, rw, q + 1, nxt);
+    if (AHEAD && q + 1 < SFM * (SFN / 2)) s_dh_load(L, T, rg, rw, q + 1, nxt);
     s_stage_pair(wl, acc[fm][2 * pr], acc[fm][2 * pr + 1]);
+    // (the pair's accumulators are free once staged)
+    if (!AHEAD) s_dh_load(L, T, rg, rw, q, cur);
     const int j = T.nt * SBN + wn * STN + pr * 64 + (lane & 7) * 8;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
@@ -434,7 +466,7 @@ __device__ __forceinline__ void s_epilogue_dh(const Layer& L, const STile& T, f3
       const uint32_t od = ok && (lane & 7) == 0 ? (uint32_t)((p * G + (j >> 6)) * 4) : OOB;
       __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(hdot), rpart, od, 0, 0);
     }
-    if (q + 1 < SFM * (SFN / 2)) cur = nxt;
+    if (AHEAD && q + 1 < SFM * (SFN / 2)) cur = nxt;
   }
 }
 
@@ -497,7 +529,7 @@ __device__ __forceinline__ void s_epilogue(const Layer& L, const STile& T, f32x1
 template <int KIND>
 __global__ __launch_bounds__(SNT) __attribute__((amdgpu_waves_per_eu(SNW / 4, SNW / 4))) void k_stream(const Layer L) {
   __shared__ __attribute__((aligned(1024))) bf16_t ring[SNS * SSTAGE];
-  __shared__ __attribute__((aligned(16))) int tokbuf[2][SBM];
+  __shared__ __attribute__((aligned(16))) int tokbuf[2][TOKB];
   __shared__ int pre[MAX_ET + 1];
   __shared__ int segst[MAX_ET + 1];
   __shared__ int sh[SNW];
@@ -511,7 +543,7 @@ __global__ __launch_bounds__(SNT) __attribute__((amdgpu_waves_per_eu(SNW / 4, SN
   const int G = gridDim.x;
   int tc = first_tile();
   if (tc >= total) return;
-  const int wid = threadIdx.x >> 6;
+  const int wid = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int rs = L.rs, r = L.r;
   const uint32_t ring_b = (uint32_t)(uintptr_t)ring;
 
@@ -532,8 +564,11 @@ __global__ __launch_bounds__(SNT) __attribute__((amdgpu_waves_per_eu(SNW / 4, SN
     if (!SP<KIND>::A_GATHER || wid != 0 || t_next >= total) return;
     const STile Tn = s_decode(pre, segst, Et, t_next, ntn);
     const int lane = threadIdx.x & 63;
-    dma16(make_desc(L.tok + Tn.row0, (int64_t)(L.Ptot - Tn.row0) * 4), (uint32_t)lane * 16u, 0,
-          __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)&tokbuf[slot][0]));
+    const int4v dt = make_desc(L.tok + Tn.row0, (int64_t)(L.Ptot - Tn.row0) * 4);
+#pragma unroll
+    for (int i = 0; i < TOKB / 256; ++i)
+      dma16(dt, (uint32_t)(i * 256 + lane * 4) * 4u, 0,
+            __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)&tokbuf[slot][256 * i]));
   };
   issue_tok(tc + G, 1);
   int gi = 0;  // global issue step (ring slot gi % SNS)
@@ -566,12 +601,20 @@ __global__ __launch_bounds__(SNT) __attribute__((amdgpu_waves_per_eu(SNW / 4, SN
   // first SPD steps of every tile but the first, the previous tile's
   // epilogue stores (issued after this tile's first stages; vector memory
   // operations retire in issue order, so counting them is exact).
-  constexpr int WAIT = (SPD - 1) * PER;
-  constexpr int WAIT_EPI = WAIT + s_epi_stores<KIND>() < 63 ? WAIT + s_epi_stores<KIND>() : 63;
+  constexpr int WAIT_HI = (SPD - 1) * PER_HI, WAIT_LO = (SPD - 1) * PER_LO;
+  constexpr int EPI = s_epi_stores<KIND>();
+  constexpr int WAIT_EPI_HI = WAIT_HI + EPI < 63 ? WAIT_HI + EPI : 63;
+  constexpr int WAIT_EPI_LO = WAIT_LO + EPI < 63 ? WAIT_LO + EPI : 63;
+  const bool hi = A_REM == 0 || wid < A_REM;  // this wave issues PER_HI per stage
   bool after_epi = false;
   auto ring_wait = [&](int c) {
-    if (after_epi && c < SPD) wait_vmcnt<WAIT_EPI>();
-    else wait_vmcnt<WAIT>();
+    if (after_epi && c < SPD) {
+      if (hi) wait_vmcnt<WAIT_EPI_HI>();
+      else wait_vmcnt<WAIT_EPI_LO>();
+    } else {
+      if (hi) wait_vmcnt<WAIT_HI>();
+      else wait_vmcnt<WAIT_LO>();
+    }
   };
 #pragma unroll 1
   for (; tc < total; tc += G) {
@@ -587,7 +630,7 @@ __global__ __launch_bounds__(SNT) __attribute__((amdgpu_waves_per_eu(SNW / 4, SN
       __syncthreads();
       issue_next();
       const bf16_t* st = ring + (gc % SNS) * SSTAGE;
-      s_mma<SP<KIND>::B_MAIN_MN>(st, st + PANEL, acc);
+      s_mma<SP<KIND>::B_MAIN_MN>(st, st + APAN, acc);
       ++gc;
     }
 #pragma unroll 1
@@ -596,7 +639,7 @@ __global__ __launch_bounds__(SNT) __attribute__((amdgpu_waves_per_eu(SNW / 4, SN
       __syncthreads();
       issue_next();
       const bf16_t* st = ring + (gc % SNS) * SSTAGE;
-      s_mma<SP<KIND>::B_LORA_MN>(st, st + PANEL, acc);
+      s_mma<SP<KIND>::B_LORA_MN>(st, st + APAN, acc);
       ++gc;
     }
     // the stage consumed last is free until the next step's issue, once
