@@ -37,6 +37,7 @@
 //    DMA'd into LDS a whole tile ahead, so building the next tile's row
 //    offsets needs no global load in the loop;
 #include <algorithm>
+#include <type_traits>
 
 #include "common.h"
 #include "gemm_util.h"
@@ -55,7 +56,7 @@ constexpr int SNW = SWM * SWN, SNT = 64 * SNW;  // 8 waves, two per SIMD
 constexpr int STM = SBM / SWM, STN = SBN / SWN; // 160 x 64 per wave
 constexpr int SFM = STM / 32, SFN = STN / 32;   // 4 x 2 fragments
 constexpr int SK = 32;                          // k per ring stage
-constexpr int SNS = 4, SPD = SNS - 1;           // ring stages, issue distance
+constexpr int SNS = 4;                          // ring stages
 constexpr int APAN = SBM * SK, BPAN = SBN * SK;  // 16-bit elements of the A and B panels
 constexpr int SSTAGE = APAN + BPAN;               // A panel then B panel
 // One DMA instruction moves 1 KiB = 16 rows of 32 k.  The B panel splits
@@ -94,13 +95,28 @@ __device__ __forceinline__ int s_kmain(const Layer& L) {
   return KIND == SK_GU || KIND == SK_DH ? L.d : KIND == SK_DN ? L.n : 2 * L.n;
 }
 
+// A work unit: a whole tile, or one column half of a tile.  With F tiles on
+// G workgroups, a last round of r = F mod G <= G / 2 tiles would leave G - r
+// workgroups idle; those r tiles run instead as 2 r half tiles (units nfull
+// .. nfull + 2 r), columns [cb, ce) of the tile, so the last round is a full
+// round of units that stream half the B panel each.
 struct STile {
-  int t, e, nt, row0, mrows;
+  int t, e, nt, row0, mrows, cb, ce;
 };
 
-__device__ __forceinline__ STile s_decode(const int* pre, const int* segst, int Et, int t, int ntn) {
+__device__ __forceinline__ STile s_decode(const int* pre, const int* segst, int Et, int u, int ntn,
+                                          int nfull) {
   STile T;
-  T.t = t;
+  T.t = u;
+  int t = u;
+  T.cb = 0;
+  T.ce = SBN;
+  if (u >= nfull) {
+    const int v = u - nfull;
+    t = nfull + (v >> 1);
+    T.cb = __builtin_amdgcn_readfirstlane((v & 1) * (SBN / 2));
+    T.ce = __builtin_amdgcn_readfirstlane(T.cb + SBN / 2);
+  }
   T.e = __builtin_amdgcn_readfirstlane(find_expert(pre, Et, t, ntn));
   const int local = t - pre[T.e] * ntn;
   const int nm = pre[T.e + 1] - pre[T.e];
@@ -110,6 +126,8 @@ __device__ __forceinline__ STile s_decode(const int* pre, const int* segst, int 
   T.mrows = __builtin_amdgcn_readfirstlane(min(SBM, segst[T.e + 1] - T.row0));
   return T;
 }
+
+__device__ __forceinline__ bool s_in(const STile& T, int c) { return c >= T.cb && c < T.ce; }
 
 // Per-lane constants of the two panel layouts.
 //  K panel, instruction j of wave w: row 16 (w + 4 j) + lane / 4, physical
@@ -187,13 +205,13 @@ __device__ __forceinline__ void s_setup(const Layer& L, const STile& T, const in
 #pragma unroll
     for (int j = 0; j < NIB; ++j) {
       const int c = s_prow(j);
-      const bool ok = j0 + (c >> 6) * 32 + (c & 31) < n;
+      const bool ok = j0 + (c >> 6) * 32 + (c & 31) < n && s_in(T, c);
       S.vb_m[j] = ok ? (uint32_t)gu_row(n, j0, c) * (uint32_t)(d * 2) + lck * 16 : OOB;
     }
     S.db_l = make_desc(L.b_gu + (int64_t)e * r * 2 * n, (int64_t)r * 2 * n * 2);
     S.ldb_bl = 2 * n * 2;
     const int c = lcm * 8;  // tile column of this lane's chunk (8 columns, one gate/up group)
-    const bool ok = j0 + (c >> 6) * 32 + (c & 31) < n;
+    const bool ok = j0 + (c >> 6) * 32 + (c & 31) < n && s_in(T, c);
 #pragma unroll
     for (int j = 0; j < NIB; ++j)
       S.vb_l[j] = ok ? (uint32_t)s_krow(j) * S.ldb_bl + (uint32_t)gu_row(n, j0, c) * 2 : OOB;
@@ -203,38 +221,44 @@ __device__ __forceinline__ void s_setup(const Layer& L, const STile& T, const in
 #pragma unroll
     for (int j = 0; j < NIB; ++j) {
       const int c = s_prow(j);
-      S.vb_m[j] = c0 + c < d ? (uint32_t)(c0 + c) * (uint32_t)(n * 2) + lck * 16 : OOB;
+      S.vb_m[j] = c0 + c < d && s_in(T, c) ? (uint32_t)(c0 + c) * (uint32_t)(n * 2) + lck * 16 : OOB;
     }
     S.db_l = make_desc(L.b_dn + (int64_t)e * r * d, (int64_t)r * d * 2);
     S.ldb_bl = d * 2;
     const int col = c0 + lcm * 8;
+    const bool cin = s_in(T, lcm * 8);
 #pragma unroll
-    for (int j = 0; j < NIB; ++j) S.vb_l[j] = col < d ? (uint32_t)s_krow(j) * S.ldb_bl + (uint32_t)col * 2 : OOB;
+    for (int j = 0; j < NIB; ++j)
+      S.vb_l[j] = col < d && cin ? (uint32_t)s_krow(j) * S.ldb_bl + (uint32_t)col * 2 : OOB;
   } else if constexpr (KIND == SK_DH) {
     const int j0 = T.nt * SBN;
     S.db_m = make_desc(L.w_dn + (int64_t)e * d * n, (int64_t)d * n * 2);
     S.ldb_bm = n * 2;
     const int col = j0 + lcm * 8;
+    const bool cin = s_in(T, lcm * 8);
 #pragma unroll
-    for (int j = 0; j < NIB; ++j) S.vb_m[j] = col < n ? (uint32_t)s_krow(j) * S.ldb_bm + (uint32_t)col * 2 : OOB;
+    for (int j = 0; j < NIB; ++j)
+      S.vb_m[j] = col < n && cin ? (uint32_t)s_krow(j) * S.ldb_bm + (uint32_t)col * 2 : OOB;
     S.db_l = make_desc(L.a_dn + (int64_t)e * n * ra, (int64_t)n * ra * 2);
 #pragma unroll
     for (int j = 0; j < NIB; ++j) {
       const int c = s_prow(j);
-      S.vb_l[j] = j0 + c < n ? (uint32_t)(j0 + c) * (uint32_t)(ra * 2) + lck * 16 : OOB;
+      S.vb_l[j] = j0 + c < n && s_in(T, c) ? (uint32_t)(j0 + c) * (uint32_t)(ra * 2) + lck * 16 : OOB;
     }
   } else {
     const int c0 = T.nt * SBN;
     S.db_m = make_desc(L.w_gu + (int64_t)e * 2 * n * d, (int64_t)2 * n * d * 2);
     S.ldb_bm = d * 2;
     const int col = c0 + lcm * 8;
+    const bool cin = s_in(T, lcm * 8);
 #pragma unroll
-    for (int j = 0; j < NIB; ++j) S.vb_m[j] = col < d ? (uint32_t)s_krow(j) * S.ldb_bm + (uint32_t)col * 2 : OOB;
+    for (int j = 0; j < NIB; ++j)
+      S.vb_m[j] = col < d && cin ? (uint32_t)s_krow(j) * S.ldb_bm + (uint32_t)col * 2 : OOB;
     S.db_l = make_desc(L.a_gu + (int64_t)e * d * ra, (int64_t)d * ra * 2);
 #pragma unroll
     for (int j = 0; j < NIB; ++j) {
       const int c = s_prow(j);
-      S.vb_l[j] = c0 + c < d ? (uint32_t)(c0 + c) * (uint32_t)(ra * 2) + lck * 16 : OOB;
+      S.vb_l[j] = c0 + c < d && s_in(T, c) ? (uint32_t)(c0 + c) * (uint32_t)(ra * 2) + lck * 16 : OOB;
     }
   }
 }
@@ -278,67 +302,98 @@ __device__ __forceinline__ void s_issue(const SIssue& S, int step, uint32_t sb, 
   }
 }
 
-// MFMAs of one ring stage, k = 32: the wave's 4 x 2 fragments.  All fragment
-// reads of the stage are issued first, then the 16 MFMAs, so the second
-// half's reads land under the first half's MFMAs and LDS latency is exposed
-// once per stage.  (Padding rows are multiplied too: branching around
-// fragments splits the accumulator's live range and the register allocator
-// then copies it through memory.)
-template <bool BMN>
-__device__ __forceinline__ void s_mma(const bf16_t* As, const bf16_t* Bs, f32x16 (&acc)[SFM][SFN]) {
+// Operand fragments of one k-half (16 k) of a ring stage: the wave's SFM A
+// fragments (rows) and SFN B fragments (columns).
+struct Frag {
+  uint4 a[SFM], b[SFN];
+};
+
+// Every LDS read of this wave has returned (gfx9 s_waitcnt: lgkmcnt 0, vmcnt
+// and expcnt left alone): a stage's slot is refilled right after the barrier
+// that follows its last reads.
+__device__ __forceinline__ void wait_lgkm0() { __builtin_amdgcn_s_waitcnt(15 | (3 << 14) | (7 << 4)); }
+
+// A fragment fm, k-half kk: row-contiguous panel, chunk c of row r stored at
+// c ^ ((r >> 2) & 3); lane L reads row wm 160 + fm 32 + L % 32, k 8 (2 kk +
+// L / 32) .. + 8.
+__device__ __forceinline__ uint4 s_read_a(const bf16_t* As, int kk, int fm) {
   const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
-  const int wm = wid / SWN, wn = wid % SWN;
-  const int l = lane & 31;
+  const int wm = wid / SWN, l = lane & 31;
   const char* ab = (const char*)As + (wm * STM + l) * (SK * 2);
-  const int swz = (l >> 2) & 3;
-  // MN panel: 16-lane group g reads k rows 8 (g >> 1) + q (+4 in the second
-  // read) at columns 16 (g & 1) + 4 rr of the fragment; the transposing read
-  // gives lane (g, j) the 4 k values of column 16 (g & 1) + j.
-  const int g = lane >> 4, q = (lane >> 2) & 3, rr = lane & 3;
-  // fragments of KB k-halves of 16 are held at once: all of the stage's
-  // (KB = 2) or one half's (KB = 1, for tiles whose accumulators leave no
-  // room for both)
-  constexpr int KB = SFM > 4 ? 1 : SK / 16;
-#pragma unroll
-  for (int k2 = 0; k2 < SK / 16; k2 += KB) {
-    uint4 a[KB][SFM], b[KB][SFN];
-#pragma unroll
-    for (int kb = 0; kb < KB; ++kb) {
-      const int kk = k2 + kb;
-      const int c = ((kk * 2 + (lane >> 5)) ^ swz) * 16;
-#pragma unroll
-      for (int fm = 0; fm < SFM; ++fm) a[kb][fm] = *(const uint4*)(ab + fm * 32 * (SK * 2) + c);
-      if constexpr (!BMN) {
-        const char* bb = (const char*)Bs + (wn * STN + l) * (SK * 2);
-#pragma unroll
-        for (int fn = 0; fn < SFN; ++fn) b[kb][fn] = *(const uint4*)(bb + fn * 32 * (SK * 2) + c);
-      } else {
-        const int krow = kk * 16 + 8 * (g >> 1) + q;
-        const int kx = (krow & 3) * 4;
-#pragma unroll
-        for (int fn = 0; fn < SFN; ++fn) {
-          const int col = wn * STN + fn * 32 + 16 * (g & 1) + 4 * rr;
-          const char* p = (const char*)Bs + krow * (SBN * 2) + (((col >> 3) ^ kx) * 16) + (col & 7) * 2;
-          const v4s lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s*)p);
-          const v4s hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s*)(p + 4 * SBN * 2));
-          b[kb][fn] = make_uint4((uint32_t)(uint16_t)lo[0] | ((uint32_t)(uint16_t)lo[1] << 16),
-                                 (uint32_t)(uint16_t)lo[2] | ((uint32_t)(uint16_t)lo[3] << 16),
-                                 (uint32_t)(uint16_t)hi[0] | ((uint32_t)(uint16_t)hi[1] << 16),
-                                 (uint32_t)(uint16_t)hi[2] | ((uint32_t)(uint16_t)hi[3] << 16));
-        }
-      }
-    }
-#pragma unroll
-    for (int kb = 0; kb < KB; ++kb)
-#pragma unroll
-      for (int fm = 0; fm < SFM; ++fm)
-#pragma unroll
-        for (int fn = 0; fn < SFN; ++fn) acc[fm][fn] = mfma32(b[kb][fn], a[kb][fm], acc[fm][fn]);
-    // keep that order: the LDS reads of the group, then its MFMAs
-    constexpr int NREAD = KB * (SFM + (BMN ? 2 : 1) * SFN);
-    __builtin_amdgcn_sched_group_barrier(0x100, NREAD, 0);
-    __builtin_amdgcn_sched_group_barrier(0x008, KB * SFM * SFN, 0);
+  const int c = ((kk * 2 + (lane >> 5)) ^ ((l >> 2) & 3)) * 16;
+  return *(const uint4*)(ab + fm * 32 * (SK * 2) + c);
+}
+// B fragment fn, k-half kk.  K panel: as A.  MN panel: 16-lane group g reads
+// k rows 8 (g >> 1) + q (+4 in the second read) at columns 16 (g & 1) + 4 rr
+// of the fragment; the transposing read gives lane (g, j) the 4 k values of
+// column 16 (g & 1) + j.
+template <bool BMN>
+__device__ __forceinline__ uint4 s_read_b(const bf16_t* Bs, int kk, int fn) {
+  const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
+  const int wn = wid % SWN, l = lane & 31;
+  if constexpr (!BMN) {
+    const char* bb = (const char*)Bs + (wn * STN + l) * (SK * 2);
+    const int c = ((kk * 2 + (lane >> 5)) ^ ((l >> 2) & 3)) * 16;
+    return *(const uint4*)(bb + fn * 32 * (SK * 2) + c);
+  } else {
+    const int g = lane >> 4, q = (lane >> 2) & 3, rr = lane & 3;
+    const int krow = kk * 16 + 8 * (g >> 1) + q;
+    const int kx = (krow & 3) * 4;
+    const int col = wn * STN + fn * 32 + 16 * (g & 1) + 4 * rr;
+    const char* p = (const char*)Bs + krow * (SBN * 2) + (((col >> 3) ^ kx) * 16) + (col & 7) * 2;
+    const v4s lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s*)p);
+    const v4s hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s*)(p + 4 * SBN * 2));
+    return make_uint4((uint32_t)(uint16_t)lo[0] | ((uint32_t)(uint16_t)lo[1] << 16),
+                      (uint32_t)(uint16_t)lo[2] | ((uint32_t)(uint16_t)lo[3] << 16),
+                      (uint32_t)(uint16_t)hi[0] | ((uint32_t)(uint16_t)hi[1] << 16),
+                      (uint32_t)(uint16_t)hi[2] | ((uint32_t)(uint16_t)hi[3] << 16));
   }
+}
+
+template <bool BMN>
+__device__ __forceinline__ void s_read_half(const bf16_t* st, int kk, Frag& f) {
+#pragma unroll
+  for (int fm = 0; fm < SFM; ++fm) f.a[fm] = s_read_a(st, kk, fm);
+#pragma unroll
+  for (int fn = 0; fn < SFN; ++fn) f.b[fn] = s_read_b<BMN>(st + APAN, kk, fn);
+}
+
+// The MFMAs of the k-half held in f, and into f (as its fragments fall
+// free) the reads of k-half kk of the stage at st, so that the LDS reads run
+// under the MFMAs: the MFMAs of B fragment 0 with every A fragment, the read
+// of the next B fragment 0, then those of B fragment 1 with each A fragment
+// followed by the read of that A fragment, then the read of B fragment 1.
+// The next half's first MFMA then waits only for the first two reads.
+// (Padding rows are multiplied too: branching around fragments splits the
+// accumulators' live ranges.)
+static_assert(SFN == 2, "two column fragments per wave");
+template <bool BMN_NEXT>
+__device__ __forceinline__ void s_mfma_read(Frag& f, f32x16 (&acc)[SFM][SFN], const bf16_t* st, int kk) {
+#pragma unroll
+  for (int fm = 0; fm < SFM; ++fm) acc[fm][0] = mfma32(f.b[0], f.a[fm], acc[fm][0]);
+  f.b[0] = s_read_b<BMN_NEXT>(st + APAN, kk, 0);
+#pragma unroll
+  for (int fm = 0; fm < SFM; ++fm) {
+    acc[fm][1] = mfma32(f.b[1], f.a[fm], acc[fm][1]);
+    f.a[fm] = s_read_a(st, kk, fm);
+  }
+  f.b[1] = s_read_b<BMN_NEXT>(st + APAN, kk, 1);
+  constexpr int RB = BMN_NEXT ? 2 : 1;  // LDS reads per B fragment
+  __builtin_amdgcn_sched_group_barrier(0x008, SFM, 0);
+  __builtin_amdgcn_sched_group_barrier(0x100, RB, 0);
+#pragma unroll
+  for (int fm = 0; fm < SFM; ++fm) {
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+    __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+  }
+  __builtin_amdgcn_sched_group_barrier(0x100, RB, 0);
+}
+
+__device__ __forceinline__ void s_mfma(const Frag& f, f32x16 (&acc)[SFM][SFN]) {
+#pragma unroll
+  for (int fn = 0; fn < SFN; ++fn)
+#pragma unroll
+    for (int fm = 0; fm < SFM; ++fm) acc[fm][fn] = mfma32(f.b[fn], f.a[fm], acc[fm][fn]);
 }
 
 // Epilogue, through a private 4 KiB LDS staging area per wave.  The
@@ -395,7 +450,7 @@ __device__ __forceinline__ void s_dh_load(const Layer& L, const STile& T, rsrc_t
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     const int m = wm * STM + fm * 32 + (lane >> 3) + 8 * i;
-    const bool ok = m < T.mrows && j < n;
+    const bool ok = m < T.mrows && j < n && s_in(T, wn * STN);
     const uint32_t og = ok ? (uint32_t)(((int64_t)(T.row0 + m) * 2 * n + j) * 2) : OOB;
     const auto gq = __builtin_amdgcn_raw_buffer_load_b128(rg, og, 0, 0);
     const auto uq = __builtin_amdgcn_raw_buffer_load_b128(rg, ok ? og + (uint32_t)(n * 2) : OOB, 0, 0);
@@ -432,7 +487,7 @@ __device__ __forceinline__ void s_epilogue_dh(const Layer& L, const STile& T, f3
       const uint4 v = s_unstage(wl, i);
       const uint32_t dw[4] = {v.x, v.y, v.z, v.w};
       const int m = wm * STM + fm * 32 + (lane >> 3) + 8 * i;
-      const bool ok = m < T.mrows && j < n;
+      const bool ok = m < T.mrows && j < n && s_in(T, wn * STN);
       const int64_t p = T.row0 + m;
       const uint32_t og = ok ? (uint32_t)((p * 2 * n + j) * 2) : OOB;
       const float w = cur.w[i];
@@ -502,7 +557,7 @@ __device__ __forceinline__ void s_epilogue(const Layer& L, const STile& T, f32x1
           // two lanes holding gate and up of the same j compute 4 h each
           const int c = lane & 7, up = c >> 2;
           const int j = T.nt * (SBN / 2) + (wn * (SFN / 2) + pr) * 32 + 8 * (c & 3);
-          const bool ok = m < T.mrows && j < n;
+          const bool ok = m < T.mrows && j < n && s_in(T, wn * STN);
           s_store(rg, ok ? (uint32_t)((p * 2 * n + (up ? n : 0) + j) * 2) : OOB, v);
           const uint32_t o[4] = {(uint32_t)__shfl_xor((int)v.x, 4, 64), (uint32_t)__shfl_xor((int)v.y, 4, 64),
                                  (uint32_t)__shfl_xor((int)v.z, 4, 64), (uint32_t)__shfl_xor((int)v.w, 4, 64)};
@@ -519,7 +574,7 @@ __device__ __forceinline__ void s_epilogue(const Layer& L, const STile& T, f32x1
           __builtin_amdgcn_raw_buffer_store_b64((v2u){hw[0], hw[1]}, rh, oh, 0, 0);
         } else {
           const int c = T.nt * SBN + wn * STN + pr * 64 + (lane & 7) * 8;
-          const bool ok = m < T.mrows && c < d;
+          const bool ok = m < T.mrows && c < d && s_in(T, wn * STN);
           s_store(ro, ok ? (uint32_t)((p * d + c) * 2) : OOB, v);
         }
       }
@@ -539,8 +594,11 @@ __global__ __launch_bounds__(SNT) __attribute__((amdgpu_waves_per_eu(SNW / 4, SN
   __syncthreads();
   expert_prefix<SNT>(L, pre, sh, [&](int e) { return cdiv(segst[e + 1] - segst[e], SBM); });
   const int ntn = s_ntn<KIND>(L);
-  const int total = pre[Et] * ntn;
   const int G = gridDim.x;
+  const int F = pre[Et] * ntn;  // tiles
+  const int rlast = F % G;
+  const int nsplit = rlast > 0 && 2 * rlast <= G ? rlast : 0;
+  const int nfull = F - nsplit, total = F + nsplit;  // units
   int tc = first_tile();
   if (tc >= total) return;
   const int wid = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -548,7 +606,7 @@ __global__ __launch_bounds__(SNT) __attribute__((amdgpu_waves_per_eu(SNW / 4, SN
   const uint32_t ring_b = (uint32_t)(uintptr_t)ring;
 
   // issue cursor on the first tile; its gather indices come in directly
-  STile ti = s_decode(pre, segst, Et, tc, ntn);
+  STile ti = s_decode(pre, segst, Et, tc, ntn, nfull);
   if (SP<KIND>::A_GATHER) {
     for (int m = threadIdx.x; m < SBM; m += SNT)
       tokbuf[0][m] = ti.row0 + m < L.Ptot ? L.tok[ti.row0 + m] : 0;
@@ -562,7 +620,7 @@ __global__ __launch_bounds__(SNT) __attribute__((amdgpu_waves_per_eu(SNW / 4, SN
   // the step's panels, so the step's wait covers it)
   auto issue_tok = [&](int t_next, int slot) {
     if (!SP<KIND>::A_GATHER || wid != 0 || t_next >= total) return;
-    const STile Tn = s_decode(pre, segst, Et, t_next, ntn);
+    const STile Tn = s_decode(pre, segst, Et, t_next, ntn, nfull);
     const int lane = threadIdx.x & 63;
     const int4v dt = make_desc(L.tok + Tn.row0, (int64_t)(L.Ptot - Tn.row0) * 4);
 #pragma unroll
@@ -571,15 +629,23 @@ __global__ __launch_bounds__(SNT) __attribute__((amdgpu_waves_per_eu(SNW / 4, SN
             __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)&tokbuf[slot][256 * i]));
   };
   issue_tok(tc + G, 1);
+  // the next tile's gather indices must be in before the prologue's issues
+  // can reach that tile
+  wait_vmcnt<0>();
+  __syncthreads();
   int gi = 0;  // global issue step (ring slot gi % SNS)
   auto issue_next = [&]() {
     if (S.step == S.stot) {
       const int tn = ti.t + G;
       if (!idone && tn < total) {
         ++iord;
-        ti = s_decode(pre, segst, Et, tn, ntn);
+        ti = s_decode(pre, segst, Et, tn, ntn, nfull);
         s_setup<KIND>(L, ti, tokbuf[iord & 1], S);
         issue_tok(tn + G, (iord + 1) & 1);
+        // no scalar load of the switch stays pending into the step loop
+        // (they return out of order, so a pending one would make every
+        // fragment read wait for all the others)
+        wait_lgkm0();
       } else {
         idone = true;
         S.step = S.stot - 1;
@@ -589,26 +655,31 @@ __global__ __launch_bounds__(SNT) __attribute__((amdgpu_waves_per_eu(SNW / 4, SN
     if (!idone) ++S.step;
     ++gi;
   };
+  // all SNS stages of the ring in flight before the first step
 #pragma unroll 1
-  for (int s = 0; s < SPD; ++s) issue_next();
+  for (int s = 0; s < SNS; ++s) issue_next();
 
-  // compute: tiles in order, each its base steps then its rank-r steps
+  // compute: tiles in order, each its base steps then its rank-r steps.  A
+  // step runs the MFMAs of its first k-half while reading its second; then
+  // every wave waits for the next stage and meets the others at the step's
+  // one barrier, after which the stage just read is free and is refilled;
+  // then the second half's MFMAs run while the next stage's first half is
+  // read.
   const int smain = s_kmain<KIND>(L) / SK;
-  const int slora = cdiv(rs, SK);
+  const int stot = smain + cdiv(rs, SK);
   int gc = 0;
-  // Ring wait before step c of a tile: the stage issued SPD steps earlier
-  // must be in; younger than it are the SPD - 1 later stages and, in the
-  // first SPD steps of every tile but the first, the previous tile's
-  // epilogue stores (issued after this tile's first stages; vector memory
-  // operations retire in issue order, so counting them is exact).
-  constexpr int WAIT_HI = (SPD - 1) * PER_HI, WAIT_LO = (SPD - 1) * PER_LO;
+  // The wait of step k: the stage after it must be in.  Younger than that
+  // stage are the two issued after it, and in the first two steps of every
+  // tile but the first the previous tile's epilogue stores, issued between
+  // them (vector memory operations retire in issue order).
+  constexpr int WAIT_HI = (SNS - 2) * PER_HI, WAIT_LO = (SNS - 2) * PER_LO;
   constexpr int EPI = s_epi_stores<KIND>();
   constexpr int WAIT_EPI_HI = WAIT_HI + EPI < 63 ? WAIT_HI + EPI : 63;
   constexpr int WAIT_EPI_LO = WAIT_LO + EPI < 63 ? WAIT_LO + EPI : 63;
   const bool hi = A_REM == 0 || wid < A_REM;  // this wave issues PER_HI per stage
   bool after_epi = false;
-  auto ring_wait = [&](int c) {
-    if (after_epi && c < SPD) {
+  auto ring_wait = [&](int k) {
+    if (after_epi && k < 2) {
       if (hi) wait_vmcnt<WAIT_EPI_HI>();
       else wait_vmcnt<WAIT_EPI_LO>();
     } else {
@@ -616,40 +687,63 @@ __global__ __launch_bounds__(SNT) __attribute__((amdgpu_waves_per_eu(SNW / 4, SN
       else wait_vmcnt<WAIT_LO>();
     }
   };
+  // first stage: the SNS - 1 later ones may still be in flight
+  if (hi) wait_vmcnt<(SNS - 1) * PER_HI>();
+  else wait_vmcnt<(SNS - 1) * PER_LO>();
+  __syncthreads();
+  Frag f;
+  s_read_half<SP<KIND>::B_MAIN_MN>(ring, 0, f);
+  constexpr bool MN_M = SP<KIND>::B_MAIN_MN, MN_L = SP<KIND>::B_LORA_MN;
 #pragma unroll 1
   for (; tc < total; tc += G) {
-    const STile tcur = s_decode(pre, segst, Et, tc, ntn);
     f32x16 acc[SFM][SFN];
 #pragma unroll
     for (int fm = 0; fm < SFM; ++fm)
 #pragma unroll
       for (int fn = 0; fn < SFN; ++fn) acc[fm][fn] = (f32x16)(0.0f);
-#pragma unroll 1
-    for (int k = 0; k < smain; ++k) {
+    // one step: the MFMAs of its first k-half under the reads of its second,
+    // the wait and barrier, the refill of the stage just read, the MFMAs of
+    // the second half under the reads of the next stage's first half.  The
+    // base steps, the step into the rank-r steps, and the rank-r steps are
+    // separate straight-line loops (a branch inside one would split the
+    // accumulators' live ranges).
+    auto step = [&](auto mn_cur, auto mn_next, int k) {
+      const bf16_t* st = ring + (gc % SNS) * SSTAGE;
+      s_mfma_read<decltype(mn_cur)::value>(f, acc, st, 1);
       ring_wait(k);
+      wait_lgkm0();
       __syncthreads();
       issue_next();
-      const bf16_t* st = ring + (gc % SNS) * SSTAGE;
-      s_mma<SP<KIND>::B_MAIN_MN>(st, st + APAN, acc);
+      s_mfma_read<decltype(mn_next)::value>(f, acc, ring + ((gc + 1) % SNS) * SSTAGE, 0);
       ++gc;
-    }
+    };
+    using BM = std::integral_constant<bool, MN_M>;
+    using BL = std::integral_constant<bool, MN_L>;
 #pragma unroll 1
-    for (int k = 0; k < slora; ++k) {
-      ring_wait(smain + k);
+    for (int k = 0; k < smain - 1; ++k) step(BM{}, BM{}, k);
+    step(BM{}, BL{}, smain - 1);
+#pragma unroll 1
+    for (int k = smain; k < stot - 1; ++k) step(BL{}, BL{}, k);
+    {
+      s_mfma_read<MN_L>(f, acc, ring + (gc % SNS) * SSTAGE, 1);
+      ring_wait(stot - 1);
+      wait_lgkm0();
       __syncthreads();
-      issue_next();
-      const bf16_t* st = ring + (gc % SNS) * SSTAGE;
-      s_mma<SP<KIND>::B_LORA_MN>(st, st + APAN, acc);
+      s_mfma(f, acc);
       ++gc;
     }
-    // the stage consumed last is free until the next step's issue, once
-    // every wave is done reading it
-    __syncthreads();
+    // the stage read last is not refilled until every wave has staged its
+    // outputs through it
+    const STile tcur = s_decode(pre, segst, Et, tc, ntn, nfull);
     if constexpr (KIND == SK_DH)
       s_epilogue_dh(L, tcur, acc, ring + ((gc + SNS - 1) % SNS) * SSTAGE + wid * 2048);
     else
       s_epilogue<KIND>(L, tcur, acc, ring + ((gc + SNS - 1) % SNS) * SSTAGE + wid * 2048);
     after_epi = true;
+    __syncthreads();
+    issue_next();
+    // the next tile's first half (its stage is in: the last step waited for it)
+    s_read_half<MN_M>(ring + (gc % SNS) * SSTAGE, 0, f);
   }
   wait_vmcnt<0>();
 }
