@@ -134,10 +134,13 @@ def measured_traffic(kernel: str, workload: str):
     text = open(path).read()
     m_sha = re.search(r"source_sha256:\s*([0-9a-f]{64})", text)
     m_b = re.search(r"traffic_bytes_per_launch:\s*([0-9]+)", text)
-    if not (m_sha and m_b):
+    m_src = re.search(r"source_files:\s*(.+)", text)
+    if not (m_sha and m_b and m_src):
         return None
-    src = os.path.join(ROOT, "mixture_experts_lora_amd", "csrc", "gemm.hip")
-    if hashlib.sha256(open(src, "rb").read()).hexdigest() != m_sha.group(1):
+    h = hashlib.sha256()
+    for name in m_src.group(1).split():
+        h.update(open(os.path.join(ROOT, "mixture_experts_lora_amd", "csrc", name), "rb").read())
+    if h.hexdigest() != m_sha.group(1):
         return None
     return int(m_b.group(1))
 

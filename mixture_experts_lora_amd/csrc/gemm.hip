@@ -1060,34 +1060,38 @@ __global__ __launch_bounds__(C::NT) __attribute__((amdgpu_waves_per_eu(C::OCC)))
   }
 }
 
-// For all four gradients at once (blockIdx.z = kind, blockIdx.y = expert):
-// out[e] = sum of the expert's partials in chunk order when it has >= 2
-// chunks, zeros when it has no rows; single-chunk experts were written by
-// the GEMM, so their blocks leave after one load.
-constexpr int RED_NT = 256;
+// For all four gradients at once (blockIdx.y = kind): out[e] = the sum of
+// expert e's partials in chunk order when it has >= 2 chunks, zeros when it
+// has no rows; single-chunk experts were written by the GEMM and are skipped.
+// Every block builds the per-expert chunk prefix in LDS, walks the expert
+// list and takes a grid-stride slice of each expert that needs it, so the
+// launch costs little when none does.
+constexpr int RED_NT = 256, RED_GX = 64;
 __global__ __launch_bounds__(RED_NT) void k_grad_reduce(const Layer L) {
-  const int e = blockIdx.y;
-  const int nchunk = cdiv(seg_count(L, e), SPLITK_ROWS);
-  if (nchunk == 1) return;
-  __shared__ int sh[RED_NT / 64];
-  // first partial slot of expert e: chunks of all earlier experts
-  int mine = 0;
-  for (int q = threadIdx.x; q < e; q += RED_NT) mine += cdiv(seg_count(L, q), SPLITK_ROWS);
-  int slot0;
-  block_excl_scan<RED_NT / 64>(mine, sh, &slot0);
-  const int kind = blockIdx.z;
+  const int kind = blockIdx.y;
   int M, N;
   grad_shape(kind, L.d, L.n, L.r, M, N);
   float* outbase = kind == GR_DB_DN ? L.db_dn : kind == GR_DA_DN ? L.da_dn
                  : kind == GR_DB_GU ? L.db_gu : L.da_gu;
   const float* partial = L.partial + L.partial_off[kind];
   const int64_t MN = (int64_t)M * N;
-  float* out = outbase + (int64_t)e * MN;
-  for (int64_t i = (int64_t)blockIdx.x * RED_NT + threadIdx.x; i < MN;
-       i += (int64_t)gridDim.x * RED_NT) {
-    float acc = 0.0f;
-    for (int c = 0; c < nchunk; ++c) acc += partial[(int64_t)(slot0 + c) * MN + i];
-    out[i] = acc;
+  // first partial slot of every expert (chunks of the experts before it)
+  __shared__ int pre[MAX_ET + 1];
+  __shared__ int sh[RED_NT / 64];
+  expert_prefix<RED_NT>(L, pre, sh, [&](int e) { return cdiv(seg_count(L, e), SPLITK_ROWS); });
+  // usually every expert has exactly one chunk: then nothing is left to do
+  int need = 0;
+  for (int e = threadIdx.x; e < L.Et; e += RED_NT) need |= pre[e + 1] - pre[e] != 1;
+  if (!__syncthreads_or(need)) return;
+  for (int e = 0; e < L.Et; ++e) {
+    const int slot0 = pre[e], nchunk = pre[e + 1] - slot0;
+    if (nchunk == 1) continue;
+    float* out = outbase + (int64_t)e * MN;
+    for (int64_t i = (int64_t)blockIdx.x * RED_NT + threadIdx.x; i < MN; i += (int64_t)gridDim.x * RED_NT) {
+      float acc = 0.0f;
+      for (int c = 0; c < nchunk; ++c) acc += partial[(int64_t)(slot0 + c) * MN + i];
+      out[i] = acc;
+    }
   }
 }
 
@@ -1234,8 +1238,8 @@ hipError_t gemm_lora_grads(const Layer& L, hipStream_t st) {
     grad_shape(kind, L.d, L.n, L.r, M, N);
     mn_max = std::max<int64_t>(mn_max, (int64_t)M * N);
   }
-  const int gx = (int)std::min<int64_t>(cdiv64(mn_max, RED_NT), 32);
-  MOE_LAUNCH("reduce_grads", k_grad_reduce, dim3(gx, L.Et, 4), dim3(RED_NT), 0, st, L);
+  const int gx = (int)std::min<int64_t>(cdiv64(mn_max, RED_NT), RED_GX);
+  MOE_LAUNCH("reduce_grads", k_grad_reduce, dim3(gx, 4), dim3(RED_NT), 0, st, L);
   return hipGetLastError();
 }
 
