@@ -157,7 +157,7 @@ struct SIssue {
   int4v da_m, db_m, da_l, db_l;
   uint32_t va_m[NIA], vb_m[NIB], va_l[NIA], vb_l[NIB];
   uint32_t ldb_bm, ldb_bl;  // byte stride of the MN-panel sources (k rows)
-  int step, smain, stot;
+  int step, smain, stot, rot;
 };
 
 template <int KIND>
@@ -168,6 +168,12 @@ __device__ __forceinline__ void s_setup(const Layer& L, const STile& T, const in
   S.smain = s_kmain<KIND>(L) / SK;
   S.stot = S.smain + cdiv(rs, SK);
   S.step = 0;
+  // Each tile starts its base K loop at step 2 e of its expert e (wrapping
+  // round; a step is 32 k, 64 bytes of a row): the tiles in flight at one moment then
+  // read different address columns of their 4 KB-strided rows instead of all
+  // of them the same one.  Every tile of an expert keeps the same order, so
+  // the N tiles that share an A panel still stream it in step.
+  S.rot = __builtin_amdgcn_readfirstlane((2 * T.e) % S.smain);
   S.ldb_bm = 0;
   S.ldb_bl = 0;
   // A main
@@ -273,7 +279,9 @@ __device__ __forceinline__ void s_issue(const SIssue& S, int step, uint32_t sb, 
   // waves at A_FULL
   auto a_on = [&](int j) { return j < A_FULL || wid < A_REM; };
   if (step < S.smain) {
-    const int k0 = step * SK;
+    int ks = step + S.rot;
+    if (ks >= S.smain) ks -= S.smain;
+    const int k0 = ks * SK;
 #pragma unroll
     for (int j = 0; j < NIA; ++j)
       if (a_on(j))
