@@ -9,6 +9,8 @@ Prints ONE JSON line.  Besides the driver's fields it carries
   roofline      the dominant kernel (the gate_up grouped GEMM) against its
                 bound, from HIP-event timing of every launch over a second
                 timed region of the same steps;
+  step_roofline the whole step against max(FLOPs / MFMA peak, minimum
+                bytes / HBM peak);
   gemm_mfma_frac  algorithmic grouped-GEMM FLOPs / summed GEMM kernel time /
                 bf16 dense MFMA peak;
   kernels_us    average duration per kernel;
@@ -82,6 +84,28 @@ def kernel_work(c):
     four = [work[g] for g in ("grad_db_dn", "grad_da_dn", "grad_db_gu", "grad_da_gu")]
     work["lora_grads"] = (sum(f for f, _ in four), sum(b for _, b in four))
     return work
+
+
+def step_roofline(c, ms):
+    """The whole step (route + forward + backward) against its roofline:
+    t_roof = max(algorithmic FLOPs / bf16 peak, minimum bytes / HBM peak).
+
+    FLOPs: forward 6 P d n + 2 P r (2d + 3n), backward 6 P d n + 4 P r (2d + 3n)
+    (no base-weight gradient; each X A / H A product once).  Minimum bytes:
+    logits once, X twice, dY once, W_gu and W_dn twice, the LoRA factors
+    twice, G and the rank-r saves written and read, Y and dX written, the
+    fp32 LoRA gradients written."""
+    T, d, n, r, k, S, E = c.T, c.d, c.n, c.r, c.k, c.n_shared, c.E
+    P, Et, b = T * k + S * T, E + S, 2
+    flops = (6 * P * d * n + 2 * P * r * (2 * d + 3 * n)) + (6 * P * d * n + 4 * P * r * (2 * d + 3 * n))
+    lora = Et * r * (d + 2 * n + n + d)
+    byts = (T * E * 4 + 3 * T * d * b + 2 * Et * 3 * n * d * b + 2 * lora * b
+            + 2 * P * 2 * n * b + 2 * 2 * P * r * b + 2 * T * d * b + lora * 4)
+    t_f, t_b = flops / PEAK_BF16, byts / PEAK_HBM
+    t_roof = max(t_f, t_b)
+    return {"bound": "hbm" if t_b >= t_f else "mfma", "t_roof_us": round(t_roof * 1e6, 1),
+            "t_us": round(ms * 1e3, 1), "frac": t_roof / (ms * 1e-3),
+            "algorithmic_flops": flops, "min_bytes": byts}
 
 
 def cpu_baseline(dims, inp, budget_s: float):
@@ -312,6 +336,7 @@ def main():
         "gemm_mfma_frac": gemm_flops / gemm_time / PEAK_BF16,
         "gemm_tflops": gemm_flops / gemm_time / 1e12,
         "roofline": roof,
+        "step_roofline": step_roofline(c, ms),
         "kernels_us": {k: round(v, 2) for k, v in sorted(avg_us.items())},
         "memory_bound_kernels": mem,
         "router_grads": router,
