@@ -3,7 +3,8 @@ checked against the oracle on outputs it can compute one by one: Y, dX and
 router-gradient rows of sampled tokens (float64), and the LoRA gradients of
 sampled experts (float32: the least-loaded expert with rows, an empty expert
 when there is one, the most-loaded expert, and the shared expert when there
-is one).  The headline shape runs again with fp16 elements.
+is one), and a rerun in the same buffers must reproduce every output bit for
+bit.  The headline shape runs again with fp16 elements.
 Routing at these sizes is compared in full by test_gpu_route."""
 from dataclasses import replace
 
@@ -62,6 +63,18 @@ def test_full_size_sampled(name):
     got = [to_numpy_f64(t) for t in (g.da_gate_up, g.db_gate_up, g.da_down, g.db_down)]
     for a in got:
         assert np.all(np.isfinite(a)), "unwritten or non-finite gradient elements"
+    # a second route + forward + backward in the same buffers gives bitwise the
+    # same outputs (no atomics, no order that depends on timing)
+    first = [t.clone() for t in (y, g.dx, g.da_gate_up, g.db_gate_up, g.da_down, g.db_down,
+                                 layer.router_grads.d_topk_w, layer.router_grads.d_logits)]
+    layer.route(logits)
+    layer.forward(x)
+    layer.backward(dy, x, router=True)
+    torch.cuda.synchronize()
+    again = (layer.y, g.dx, g.da_gate_up, g.db_gate_up, g.da_down, g.db_down,
+             layer.router_grads.d_topk_w, layer.router_grads.d_logits)
+    for a, b in zip(first, again):
+        assert torch.equal(a, b), "a rerun changed an output"
     for e in sorted(experts):
         ref = oracle.lora_grads_expert(inp, ids, tw, ld, e, dtype=np.float32)
         errs = [relerr(a[e], b) if np.any(b) else float(np.max(np.abs(a[e]))) for a, b in zip(got, ref)]
