@@ -5,7 +5,7 @@ One step = route + forward + backward of the Qwen3-30B-A3B-shaped layer
 (T=4096, d=2048, n=768, E=128, top-8, LoRA rank 64 on gate_up and down, bf16,
 router logits N(0,1)) on seeded synthetic inputs already resident in HBM.
 
-Prints ONE JSON line.  Besides the driver's fields it carries
+Prints ONE JSON line.  Besides the standard benchmark fields it carries
   roofline      the dominant kernel (the gate_up grouped GEMM) against its
                 bound, from HIP-event timing of every launch over a second
                 timed region of the same steps;
