@@ -19,17 +19,31 @@ __global__ __launch_bounds__(256) void k_combine(const Layer L, int weighted,
     float acc[8];
 #pragma unroll
     for (int q = 0; q < 8; ++q) acc[q] = 0.0f;
-    for (int j = 0; j < k; ++j) {
-      const int64_t i = (int64_t)t * k + j;
-      const int64_t p = L.pair_pos[i];
-      const float w = weighted ? L.topk_w[i] : 1.0f;
-      const uint4 v = *(const uint4*)(src + p * d + c);
+    auto add = [&](const uint4& v, float w) {
       const uint32_t u[4] = {v.x, v.y, v.z, v.w};
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
         acc[2 * q] += w * bf2f((bf16_t)(u[q] & 0xffffu));
         acc[2 * q + 1] += w * bf2f((bf16_t)(u[q] >> 16));
       }
+    };
+    // four slots' rows in flight at once, added in slot order
+    int j = 0;
+    for (; j + 4 <= k; j += 4) {
+      uint4 v[4];
+      float w[4];
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int64_t i = (int64_t)t * k + j + q;
+        w[q] = weighted ? L.topk_w[i] : 1.0f;
+        v[q] = *(const uint4*)(src + (int64_t)L.pair_pos[i] * d + c);
+      }
+#pragma unroll
+      for (int q = 0; q < 4; ++q) add(v[q], w[q]);
+    }
+    for (; j < k; ++j) {
+      const int64_t i = (int64_t)t * k + j;
+      add(*(const uint4*)(src + (int64_t)L.pair_pos[i] * d + c), weighted ? L.topk_w[i] : 1.0f);
     }
     if (L.S) {
       const uint4 v = *(const uint4*)(src + ((int64_t)L.P + t) * d + c);
