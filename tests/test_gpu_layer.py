@@ -2,7 +2,7 @@
 element, at sizes the oracle finishes in seconds: several M/N tiles, ragged
 segment tails, ranks that are and are not multiples of 8, a shared expert, a
 LoRA scale other than 1, empty experts, split-K LoRA gradients, k = E, k = 1,
-T = 1; the routing-weight and logit gradients with every case; every case
+T = 1, the largest expert count (256 with the shared one); the routing-weight and logit gradients with every case; every case
 again with fp16 elements.
 
 Every output buffer is filled with NaN before the call (an unwritten element
@@ -33,6 +33,8 @@ CASES = {
     "wide_d320_zipf": LayerDims(700, 320, 192, 8, 3, 24, logits_recipe="zipf"),
     # contraction long enough for the rank-r pre-passes to split over workgroups
     "prepass_splits": LayerDims(200, 1024, 256, 4, 2, 16),
+    # the most experts the library takes: 255 routed + 1 shared = 256, most of them empty or tiny
+    "max_experts_255_shared": LayerDims(600, 64, 64, 255, 4, 8, n_shared=1),
 }
 CASES.update({f"{k}_f16": replace(v, element="f16") for k, v in list(CASES.items())})
 
