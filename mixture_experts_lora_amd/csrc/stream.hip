@@ -8,12 +8,20 @@
 // added into the same accumulator ("Faster LoRA MoE training").
 //
 // One persistent workgroup per CU runs ONE pipeline over its whole work
-// list: every step moves a 32-k panel of each operand (320 rows of A, 256
+// list: every step moves a k panel of each operand (320 rows of A, 256
 // columns of B) from global memory straight into LDS (buffer_load_dwordx4
-// ... lds), through a ring of four stages issued three steps ahead.  The step stream runs through a tile's
-// base K steps, then its rank-r steps, then on into the next tile, so the
-// pipeline never drains between tiles: the next tile's first panels are in
-// flight while the current tile's epilogue writes its outputs.
+// ... lds).  The step stream runs through a tile's base K steps, then its
+// rank-r steps, then on into the next tile, so the pipeline never drains
+// between tiles: the next tile's first panels are in flight while the
+// current tile's epilogue writes its outputs.
+//
+// The file is compiled twice, once per stage depth MOE_SK:
+//  - 32 k per stage, a ring of four stages issued three steps ahead, for
+//    gate_up (with 64-k stages its nine DMA offsets per stage and the SwiGLU
+//    epilogue's registers do not fit beside the accumulators);
+//  - 64 k per stage, two stages, for down, dh and dx: every row of a
+//    row-contiguous panel is then one whole 128-byte line per request, half
+//    the L1->L2 requests of 32-k stages for the same bytes.
 //
 //  - tile 320 x 256, 8 waves of 160 x 64, two per SIMD
 //    (v_mfma_f32_32x32x16 on bf16 or fp16, fp32 accumulation, operands
@@ -24,11 +32,13 @@
 //    and with about 256 +- 16 rows per expert a 256-row tile leaves half the
 //    experts a short tail tile that streams the expert's whole weight panel
 //    again for a few rows; 320 covers such an expert in one tile;
-//  - row-contiguous panels are stored [rows][32 k] with the 16-byte chunk
-//    of row r at position c ^ ((r >> 2) & 3), read with ds_read_b128;
+//  - row-contiguous panels are stored [rows][SK k] with the 16-byte chunk
+//    of row r at position c ^ ((r >> 2) & 3) (32 k) or c ^ ((r >> 1) & 7)
+//    (64 k), so that the 16 rows a quarter-wave of ds_read_b128 reads fall
+//    on 16 distinct 16-byte bank groups;
 //  - panels whose contraction index is the row index in memory (W_dn and
 //    W_gu in the backward, B_dn and B_gu in the forward) are stored
-//    [32 k][256 columns] with chunk c of row k at c ^ 4 (k & 3), and read
+//    [SK k][256 columns] with chunk c of row k at c ^ 4 (k & 3), and read
 //    with ds_read_b64_tr_b16, which hands each lane 4 consecutive k of one
 //    column: two of them make one MFMA operand;
 //  - rows past a segment, columns past a matrix and k past the rank get an
@@ -55,14 +65,20 @@ constexpr int SWM = 2, SWN = 4;                 // wave grid
 constexpr int SNW = SWM * SWN, SNT = 64 * SNW;  // 8 waves, two per SIMD
 constexpr int STM = SBM / SWM, STN = SBN / SWN; // 160 x 64 per wave
 constexpr int SFM = STM / 32, SFN = STN / 32;   // 4 x 2 fragments
-constexpr int SK = 32;                          // k per ring stage
-constexpr int SNS = 4;                          // ring stages
+#ifndef MOE_SK
+#error "compile with -DMOE_SK=32 (gate_up) or -DMOE_SK=64 (down, dh, dx)"
+#endif
+constexpr int SK = MOE_SK;                      // k per ring stage
+constexpr int SNS = SK == 64 ? 2 : 4;           // ring stages
+constexpr int HK = SK / 16;                     // 16-k halves per stage
+constexpr int CPR = SK / 8;                     // 16-byte chunks per K-panel row
+constexpr int RPI = 1024 / (SK * 2);            // K-panel rows per DMA instruction
 constexpr int APAN = SBM * SK, BPAN = SBN * SK;  // 16-bit elements of the A and B panels
 constexpr int SSTAGE = APAN + BPAN;               // A panel then B panel
-// One DMA instruction moves 1 KiB = 16 rows of 32 k.  The B panel splits
+// One DMA instruction moves 1 KiB = RPI rows of SK k.  The B panel splits
 // evenly over the waves; the A panel's AIN instructions go A_FULL to every
 // wave and one more to each of the first A_REM waves.
-constexpr int AIN = SBM / 16, BIN = SBN / 16;
+constexpr int AIN = SBM / RPI, BIN = SBN / RPI;
 constexpr int A_FULL = AIN / SNW, A_REM = AIN % SNW;
 constexpr int NIA = A_FULL + (A_REM ? 1 : 0), NIB = BIN / SNW;
 constexpr int PER_HI = NIA + NIB, PER_LO = A_FULL + NIB;  // per wave per stage
@@ -130,13 +146,19 @@ __device__ __forceinline__ STile s_decode(const int* pre, const int* segst, int 
 __device__ __forceinline__ bool s_in(const STile& T, int c) { return c >= T.cb && c < T.ce; }
 
 // Per-lane constants of the two panel layouts.
-//  K panel, instruction j of wave w: row 16 (w + 4 j) + lane / 4, physical
-//  chunk lane % 4 holding logical chunk lck = (lane & 3) ^ ((lane >> 4) & 3).
-//  MN panel, instruction j of wave w: k row 2 (w + 4 j) + lane / 32, physical
+//  K panel, instruction j of wave w: row RPI (w + 8 j) + lane / CPR,
+//  physical chunk lane % CPR holding logical chunk s_lck(j) = physical ^
+//  the row's swizzle.
+//  MN panel, instruction j of wave w: k row 2 (w + 8 j) + lane / 32, physical
 //  chunk lane % 32 holding logical chunk lcm = (lane & 31) ^ fsw.
-__device__ __forceinline__ int s_lck() {
+__device__ __forceinline__ int s_kswz(int r) { return SK == 32 ? (r >> 2) & 3 : (r >> 1) & 7; }
+__device__ __forceinline__ int s_prow(int j) {
+  const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
+  return RPI * (wid + j * SNW) + lane / CPR;
+}
+__device__ __forceinline__ int s_lck(int j) {
   const int lane = threadIdx.x & 63;
-  return (lane & 3) ^ ((lane >> 4) & 3);
+  return (lane % CPR) ^ s_kswz(s_prow(j));
 }
 __device__ __forceinline__ int s_lcm() {
   const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
@@ -145,10 +167,6 @@ __device__ __forceinline__ int s_lcm() {
 __device__ __forceinline__ int s_krow(int j) {
   const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
   return 2 * (wid + j * SNW) + (lane >> 5);
-}
-__device__ __forceinline__ int s_prow(int j) {
-  const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
-  return 16 * (wid + j * SNW) + (lane >> 2);
 }
 
 // Issue cursor: the tile whose panels are being issued, its descriptors and
@@ -163,7 +181,7 @@ struct SIssue {
 template <int KIND>
 __device__ __forceinline__ void s_setup(const Layer& L, const STile& T, const int* tok, SIssue& S) {
   const int n = L.n, d = L.d, rs = L.rs, ra = L.ra, r = L.r;
-  const int lck = s_lck(), lcm = s_lcm();
+  const int lcm = s_lcm();
   const int e = T.e, row0 = T.row0, mrows = T.mrows;
   S.smain = s_kmain<KIND>(L) / SK;
   S.stot = S.smain + cdiv(rs, SK);
@@ -173,7 +191,7 @@ __device__ __forceinline__ void s_setup(const Layer& L, const STile& T, const in
   // read different address columns of their 4 KB-strided rows instead of all
   // of them the same one.  Every tile of an expert keeps the same order, so
   // the N tiles that share an A panel still stream it in step.
-  S.rot = __builtin_amdgcn_readfirstlane((2 * T.e) % S.smain);
+  S.rot = __builtin_amdgcn_readfirstlane((T.e * (64 / SK)) % S.smain);
   S.ldb_bm = 0;
   S.ldb_bl = 0;
   // A main
@@ -182,7 +200,7 @@ __device__ __forceinline__ void s_setup(const Layer& L, const STile& T, const in
 #pragma unroll
     for (int j = 0; j < NIA; ++j) {
       const int m = s_prow(j);
-      S.va_m[j] = m < mrows ? (uint32_t)tok[m] * (uint32_t)(d * 2) + lck * 16 : OOB;
+      S.va_m[j] = m < mrows ? (uint32_t)tok[m] * (uint32_t)(d * 2) + s_lck(j) * 16 : OOB;
     }
   } else {
     const int lda = KIND == SK_DN ? n : 2 * n;
@@ -191,7 +209,7 @@ __device__ __forceinline__ void s_setup(const Layer& L, const STile& T, const in
 #pragma unroll
     for (int j = 0; j < NIA; ++j) {
       const int m = s_prow(j);
-      S.va_m[j] = m < mrows ? (uint32_t)m * (uint32_t)(lda * 2) + lck * 16 : OOB;
+      S.va_m[j] = m < mrows ? (uint32_t)m * (uint32_t)(lda * 2) + s_lck(j) * 16 : OOB;
     }
   }
   // A rank-r
@@ -201,7 +219,7 @@ __device__ __forceinline__ void s_setup(const Layer& L, const STile& T, const in
 #pragma unroll
     for (int j = 0; j < NIA; ++j) {
       const int m = s_prow(j);
-      S.va_l[j] = m < mrows ? (uint32_t)m * (uint32_t)(rs * 2) + lck * 16 : OOB;
+      S.va_l[j] = m < mrows ? (uint32_t)m * (uint32_t)(rs * 2) + s_lck(j) * 16 : OOB;
     }
   }
   // B main and B rank-r
@@ -212,7 +230,7 @@ __device__ __forceinline__ void s_setup(const Layer& L, const STile& T, const in
     for (int j = 0; j < NIB; ++j) {
       const int c = s_prow(j);
       const bool ok = j0 + (c >> 6) * 32 + (c & 31) < n && s_in(T, c);
-      S.vb_m[j] = ok ? (uint32_t)gu_row(n, j0, c) * (uint32_t)(d * 2) + lck * 16 : OOB;
+      S.vb_m[j] = ok ? (uint32_t)gu_row(n, j0, c) * (uint32_t)(d * 2) + s_lck(j) * 16 : OOB;
     }
     S.db_l = make_desc(L.b_gu + (int64_t)e * r * 2 * n, (int64_t)r * 2 * n * 2);
     S.ldb_bl = 2 * n * 2;
@@ -227,7 +245,7 @@ __device__ __forceinline__ void s_setup(const Layer& L, const STile& T, const in
 #pragma unroll
     for (int j = 0; j < NIB; ++j) {
       const int c = s_prow(j);
-      S.vb_m[j] = c0 + c < d && s_in(T, c) ? (uint32_t)(c0 + c) * (uint32_t)(n * 2) + lck * 16 : OOB;
+      S.vb_m[j] = c0 + c < d && s_in(T, c) ? (uint32_t)(c0 + c) * (uint32_t)(n * 2) + s_lck(j) * 16 : OOB;
     }
     S.db_l = make_desc(L.b_dn + (int64_t)e * r * d, (int64_t)r * d * 2);
     S.ldb_bl = d * 2;
@@ -249,7 +267,7 @@ __device__ __forceinline__ void s_setup(const Layer& L, const STile& T, const in
 #pragma unroll
     for (int j = 0; j < NIB; ++j) {
       const int c = s_prow(j);
-      S.vb_l[j] = j0 + c < n && s_in(T, c) ? (uint32_t)(j0 + c) * (uint32_t)(ra * 2) + lck * 16 : OOB;
+      S.vb_l[j] = j0 + c < n && s_in(T, c) ? (uint32_t)(j0 + c) * (uint32_t)(ra * 2) + s_lck(j) * 16 : OOB;
     }
   } else {
     const int c0 = T.nt * SBN;
@@ -264,7 +282,7 @@ __device__ __forceinline__ void s_setup(const Layer& L, const STile& T, const in
 #pragma unroll
     for (int j = 0; j < NIB; ++j) {
       const int c = s_prow(j);
-      S.vb_l[j] = c0 + c < d && s_in(T, c) ? (uint32_t)(c0 + c) * (uint32_t)(ra * 2) + lck * 16 : OOB;
+      S.vb_l[j] = c0 + c < d && s_in(T, c) ? (uint32_t)(c0 + c) * (uint32_t)(ra * 2) + s_lck(j) * 16 : OOB;
     }
   }
 }
@@ -292,11 +310,10 @@ __device__ __forceinline__ void s_issue(const SIssue& S, int step, uint32_t sb, 
             __builtin_amdgcn_readfirstlane(mb + (wid + j * SNW) * 1024));
   } else {
     const int k0 = (step - S.smain) * SK;
-    const int kc = s_lck() * 8;
 #pragma unroll
     for (int j = 0; j < NIA; ++j)
       if (a_on(j))
-        dma16(S.da_l, k0 + kc < rs ? S.va_l[j] : OOB, (uint32_t)k0 * 2u,
+        dma16(S.da_l, k0 + s_lck(j) * 8 < rs ? S.va_l[j] : OOB, (uint32_t)k0 * 2u,
               __builtin_amdgcn_readfirstlane(ma + (wid + j * SNW) * 1024));
 #pragma unroll
     for (int j = 0; j < NIB; ++j) {
@@ -304,7 +321,7 @@ __device__ __forceinline__ void s_issue(const SIssue& S, int step, uint32_t sb, 
         dma16(S.db_l, k0 + s_krow(j) < r ? S.vb_l[j] : OOB, (uint32_t)k0 * S.ldb_bl,
               __builtin_amdgcn_readfirstlane(mb + (wid + j * SNW) * 1024));
       else
-        dma16(S.db_l, k0 + kc < rs ? S.vb_l[j] : OOB, (uint32_t)k0 * 2u,
+        dma16(S.db_l, k0 + s_lck(j) * 8 < rs ? S.vb_l[j] : OOB, (uint32_t)k0 * 2u,
               __builtin_amdgcn_readfirstlane(mb + (wid + j * SNW) * 1024));
     }
   }
@@ -328,7 +345,7 @@ __device__ __forceinline__ uint4 s_read_a(const bf16_t* As, int kk, int fm) {
   const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
   const int wm = wid / SWN, l = lane & 31;
   const char* ab = (const char*)As + (wm * STM + l) * (SK * 2);
-  const int c = ((kk * 2 + (lane >> 5)) ^ ((l >> 2) & 3)) * 16;
+  const int c = ((kk * 2 + (lane >> 5)) ^ s_kswz(l)) * 16;
   return *(const uint4*)(ab + fm * 32 * (SK * 2) + c);
 }
 // B fragment fn, k-half kk.  K panel: as A.  MN panel: 16-lane group g reads
@@ -341,7 +358,7 @@ __device__ __forceinline__ uint4 s_read_b(const bf16_t* Bs, int kk, int fn) {
   const int wn = wid % SWN, l = lane & 31;
   if constexpr (!BMN) {
     const char* bb = (const char*)Bs + (wn * STN + l) * (SK * 2);
-    const int c = ((kk * 2 + (lane >> 5)) ^ ((l >> 2) & 3)) * 16;
+    const int c = ((kk * 2 + (lane >> 5)) ^ s_kswz(l)) * 16;
     return *(const uint4*)(bb + fn * 32 * (SK * 2) + c);
   } else {
     const int g = lane >> 4, q = (lane >> 2) & 3, rr = lane & 3;
@@ -682,8 +699,8 @@ __global__ __launch_bounds__(SNT) __attribute__((amdgpu_waves_per_eu(SNW / 4, SN
   // them (vector memory operations retire in issue order).
   constexpr int WAIT_HI = (SNS - 2) * PER_HI, WAIT_LO = (SNS - 2) * PER_LO;
   constexpr int EPI = s_epi_stores<KIND>();
-  constexpr int WAIT_EPI_HI = WAIT_HI + EPI < 63 ? WAIT_HI + EPI : 63;
-  constexpr int WAIT_EPI_LO = WAIT_LO + EPI < 63 ? WAIT_LO + EPI : 63;
+  constexpr int WAIT_EPI_HI = SNS == 2 ? 0 : WAIT_HI + EPI < 63 ? WAIT_HI + EPI : 63;
+  constexpr int WAIT_EPI_LO = SNS == 2 ? 0 : WAIT_LO + EPI < 63 ? WAIT_LO + EPI : 63;
   const bool hi = A_REM == 0 || wid < A_REM;  // this wave issues PER_HI per stage
   bool after_epi = false;
   auto ring_wait = [&](int k) {
@@ -717,7 +734,8 @@ __global__ __launch_bounds__(SNT) __attribute__((amdgpu_waves_per_eu(SNW / 4, SN
     // accumulators' live ranges).
     auto step = [&](auto mn_cur, auto mn_next, int k) {
       const bf16_t* st = ring + (gc % SNS) * SSTAGE;
-      s_mfma_read<decltype(mn_cur)::value>(f, acc, st, 1);
+#pragma unroll
+      for (int kk = 1; kk < HK; ++kk) s_mfma_read<decltype(mn_cur)::value>(f, acc, st, kk);
       ring_wait(k);
       wait_lgkm0();
       __syncthreads();
@@ -733,7 +751,8 @@ __global__ __launch_bounds__(SNT) __attribute__((amdgpu_waves_per_eu(SNW / 4, SN
 #pragma unroll 1
     for (int k = smain; k < stot - 1; ++k) step(BL{}, BL{}, k);
     {
-      s_mfma_read<MN_L>(f, acc, ring + (gc % SNS) * SSTAGE, 1);
+#pragma unroll
+      for (int kk = 1; kk < HK; ++kk) s_mfma_read<MN_L>(f, acc, ring + (gc % SNS) * SSTAGE, kk);
       ring_wait(stot - 1);
       wait_lgkm0();
       __syncthreads();
@@ -768,10 +787,13 @@ static hipError_t launch_stream(const Layer& L, hipStream_t st, const char* name
   return hipGetLastError();
 }
 
+#if MOE_SK == 32
 hipError_t stream_gate_up(const Layer& L, hipStream_t st) { return launch_stream<SK_GU>(L, st, "gate_up"); }
+#else
 hipError_t stream_down(const Layer& L, hipStream_t st) { return launch_stream<SK_DN>(L, st, "down"); }
 hipError_t stream_dx(const Layer& L, hipStream_t st) { return launch_stream<SK_DX>(L, st, "dx"); }
 hipError_t stream_dh(const Layer& L, hipStream_t st) { return launch_stream<SK_DH>(L, st, "dh"); }
+#endif
 
 }  // inline namespace MOE_EL
 }  // namespace moe
