@@ -64,7 +64,7 @@ constexpr int SBM = MOE_SBM, SBN = 256;         // tile
 constexpr int SWM = 2, SWN = 4;                 // wave grid
 constexpr int SNW = SWM * SWN, SNT = 64 * SNW;  // 8 waves, two per SIMD
 constexpr int STM = SBM / SWM, STN = SBN / SWN; // 160 x 64 per wave
-constexpr int SFM = STM / 32, SFN = STN / 32;   // 4 x 2 fragments
+constexpr int SFM = STM / 32, SFN = STN / 32;   // 5 x 2 fragments
 #ifndef MOE_SK
 #error "compile with -DMOE_SK=32 (gate_up) or -DMOE_SK=64 (down, dh, dx)"
 #endif
@@ -186,11 +186,12 @@ __device__ __forceinline__ void s_setup(const Layer& L, const STile& T, const in
   S.smain = s_kmain<KIND>(L) / SK;
   S.stot = S.smain + cdiv(rs, SK);
   S.step = 0;
-  // Each tile starts its base K loop at step 2 e of its expert e (wrapping
-  // round; a step is 32 k, 64 bytes of a row): the tiles in flight at one moment then
-  // read different address columns of their 4 KB-strided rows instead of all
-  // of them the same one.  Every tile of an expert keeps the same order, so
-  // the N tiles that share an A panel still stream it in step.
+  // Each tile starts its base K loop 64 e k into the contraction of its
+  // expert e (wrapping round; 128 bytes of a row per expert, at either stage
+  // depth): the tiles in flight at one moment then read different address
+  // columns of their 4 KB-strided rows instead of all of them the same one.
+  // Every tile of an expert keeps the same order, so the N tiles that share
+  // an A panel still stream it in step.
   S.rot = __builtin_amdgcn_readfirstlane((T.e * (64 / SK)) % S.smain);
   S.ldb_bm = 0;
   S.ldb_bl = 0;
