@@ -17,13 +17,10 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 OBJ = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libmoe_lora.so")
-SOURCES = ("api.hip", "route.hip", "gemm.hip", "prepass.hip", "grads.hip", "combine.hip",
+SOURCES = ("api.hip", "route.hip", "gemm.hip", "stream.hip", "prepass.hip", "grads.hip", "combine.hip",
            "layer.hip", "tune.hip", "timing.hip")
-# the streamed products, once per stage depth: 32 k for gate_up, 64 k for
-# down, dh and dx (flags, object suffix)
-STREAM_BUILDS = ((["-DMOE_SK=32"], "_sk32"), (["-DMOE_SK=64"], "_sk64"))
 # compiled a second time with fp16 elements (-DMOE_F16, objects *_f16.o)
-ELEMENT_SOURCES = ("gemm.hip", "prepass.hip", "grads.hip", "combine.hip")
+ELEMENT_SOURCES = ("gemm.hip", "stream.hip", "prepass.hip", "grads.hip", "combine.hip")
 ARCH = "gfx950"
 
 HIPCC_FLAGS = [
@@ -64,9 +61,6 @@ def build(extra_flags: list[str] | None = None, verbose: bool = True, out: str =
     OBJ = objdir
     os.makedirs(OBJ, exist_ok=True)
     jobs = [(s, extra, "") for s in SOURCES] + [(s, extra + ["-DMOE_F16"], "_f16") for s in ELEMENT_SOURCES]
-    for flags, suffix in STREAM_BUILDS:
-        jobs.append(("stream.hip", extra + flags, suffix))
-        jobs.append(("stream.hip", extra + flags + ["-DMOE_F16"], suffix + "_f16"))
     with cf.ThreadPoolExecutor(max_workers=min(len(jobs), 16)) as ex:
         objs = list(ex.map(lambda j: _compile(*j), jobs))
     tmp = out + ".tmp"

@@ -15,13 +15,13 @@
 // between tiles: the next tile's first panels are in flight while the
 // current tile's epilogue writes its outputs.
 //
-// The file is compiled twice, once per stage depth MOE_SK:
-//  - 32 k per stage, a ring of four stages issued three steps ahead, for
-//    gate_up (with 64-k stages its nine DMA offsets per stage and the SwiGLU
-//    epilogue's registers do not fit beside the accumulators);
-//  - 64 k per stage, two stages, for down, dh and dx: every row of a
-//    row-contiguous panel is then one whole 128-byte line per request, half
-//    the L1->L2 requests of 32-k stages for the same bytes.
+// A stage holds 64 k (MOE_SK; 32 k with a four-stage ring is the other
+// depth the code supports) in a two-stage ring: every row of a
+// row-contiguous panel is one whole 128-byte line per request, half the
+// L1->L2 requests of 32-k stages for the same bytes.  The DMA offsets that
+// are affine in the instruction index are held as one base per lane plus a
+// uniform stride, which keeps the nine instructions per stage from
+// spilling registers beside the accumulators.
 //
 //  - tile 320 x 256, 8 waves of 160 x 64, two per SIMD
 //    (v_mfma_f32_32x32x16 on bf16 or fp16, fp32 accumulation, operands
@@ -66,8 +66,9 @@ constexpr int SNW = SWM * SWN, SNT = 64 * SNW;  // 8 waves, two per SIMD
 constexpr int STM = SBM / SWM, STN = SBN / SWN; // 160 x 64 per wave
 constexpr int SFM = STM / 32, SFN = STN / 32;   // 5 x 2 fragments
 #ifndef MOE_SK
-#error "compile with -DMOE_SK=32 (gate_up) or -DMOE_SK=64 (down, dh, dx)"
+#define MOE_SK 64
 #endif
+static_assert(MOE_SK == 32 || MOE_SK == 64, "stage depth");
 constexpr int SK = MOE_SK;                      // k per ring stage
 constexpr int SNS = SK == 64 ? 2 : 4;           // ring stages
 constexpr int HK = SK / 16;                     // 16-k halves per stage
@@ -100,6 +101,13 @@ struct SP {
   static constexpr bool A_GATHER = KIND == SK_GU || KIND == SK_DH;
   static constexpr bool B_MAIN_MN = KIND == SK_DH || KIND == SK_DX;
   static constexpr bool B_LORA_MN = KIND == SK_GU || KIND == SK_DN;
+  // operands whose DMA offsets are affine in the instruction index j (a
+  // per-lane base plus j times a uniform stride): the rows of an ungathered
+  // A panel, the rank-r A rows, and every MN panel.  Rows past a tile's
+  // segment need no test there: the buffer's size ends at the segment.
+  static constexpr bool A_MAIN_AFF = !A_GATHER;
+  static constexpr bool B_MAIN_AFF = B_MAIN_MN;
+  static constexpr bool B_LORA_AFF = B_LORA_MN;
 };
 
 template <int KIND>
@@ -173,7 +181,10 @@ __device__ __forceinline__ int s_krow(int j) {
 // per-lane offsets, and the next step to issue.
 struct SIssue {
   int4v da_m, db_m, da_l, db_l;
+  // per-instruction offsets; an affine operand keeps only element 0 and
+  // adds j times its stride (xa_*, xb_*) when it issues instruction j
   uint32_t va_m[NIA], vb_m[NIB], va_l[NIA], vb_l[NIB];
+  uint32_t xa_m, xb_m, xa_l, xb_l;
   uint32_t ldb_bm, ldb_bl;  // byte stride of the MN-panel sources (k rows)
   int step, smain, stot, rot;
 };
@@ -207,21 +218,15 @@ __device__ __forceinline__ void s_setup(const Layer& L, const STile& T, const in
     const int lda = KIND == SK_DN ? n : 2 * n;
     const bf16_t* src = KIND == SK_DN ? L.h : L.dg;
     S.da_m = make_desc(src + (int64_t)row0 * lda, (int64_t)mrows * lda * 2);
-#pragma unroll
-    for (int j = 0; j < NIA; ++j) {
-      const int m = s_prow(j);
-      S.va_m[j] = m < mrows ? (uint32_t)m * (uint32_t)(lda * 2) + s_lck(j) * 16 : OOB;
-    }
+    S.va_m[0] = (uint32_t)s_prow(0) * (uint32_t)(lda * 2) + s_lck(0) * 16;
+    S.xa_m = (uint32_t)(RPI * SNW) * (uint32_t)(lda * 2);
   }
   // A rank-r
   {
     const bf16_t* src = KIND == SK_GU ? L.xa : KIND == SK_DN ? L.ha : KIND == SK_DH ? L.qdn : L.qgu;
     S.da_l = make_desc(src + (int64_t)row0 * rs, (int64_t)mrows * rs * 2);
-#pragma unroll
-    for (int j = 0; j < NIA; ++j) {
-      const int m = s_prow(j);
-      S.va_l[j] = m < mrows ? (uint32_t)m * (uint32_t)(rs * 2) + s_lck(j) * 16 : OOB;
-    }
+    S.va_l[0] = (uint32_t)s_prow(0) * (uint32_t)(rs * 2) + s_lck(0) * 16;
+    S.xa_l = (uint32_t)(RPI * SNW) * (uint32_t)(rs * 2);
   }
   // B main and B rank-r
   if constexpr (KIND == SK_GU) {
@@ -237,9 +242,8 @@ __device__ __forceinline__ void s_setup(const Layer& L, const STile& T, const in
     S.ldb_bl = 2 * n * 2;
     const int c = lcm * 8;  // tile column of this lane's chunk (8 columns, one gate/up group)
     const bool ok = j0 + (c >> 6) * 32 + (c & 31) < n && s_in(T, c);
-#pragma unroll
-    for (int j = 0; j < NIB; ++j)
-      S.vb_l[j] = ok ? (uint32_t)s_krow(j) * S.ldb_bl + (uint32_t)gu_row(n, j0, c) * 2 : OOB;
+    S.vb_l[0] = ok ? (uint32_t)s_krow(0) * S.ldb_bl + (uint32_t)gu_row(n, j0, c) * 2 : OOB;
+    S.xb_l = (uint32_t)(2 * SNW) * S.ldb_bl;
   } else if constexpr (KIND == SK_DN) {
     const int c0 = T.nt * SBN;
     S.db_m = make_desc(L.w_dn + (int64_t)e * d * n, (int64_t)d * n * 2);
@@ -252,18 +256,16 @@ __device__ __forceinline__ void s_setup(const Layer& L, const STile& T, const in
     S.ldb_bl = d * 2;
     const int col = c0 + lcm * 8;
     const bool cin = s_in(T, lcm * 8);
-#pragma unroll
-    for (int j = 0; j < NIB; ++j)
-      S.vb_l[j] = col < d && cin ? (uint32_t)s_krow(j) * S.ldb_bl + (uint32_t)col * 2 : OOB;
+    S.vb_l[0] = col < d && cin ? (uint32_t)s_krow(0) * S.ldb_bl + (uint32_t)col * 2 : OOB;
+    S.xb_l = (uint32_t)(2 * SNW) * S.ldb_bl;
   } else if constexpr (KIND == SK_DH) {
     const int j0 = T.nt * SBN;
     S.db_m = make_desc(L.w_dn + (int64_t)e * d * n, (int64_t)d * n * 2);
     S.ldb_bm = n * 2;
     const int col = j0 + lcm * 8;
     const bool cin = s_in(T, lcm * 8);
-#pragma unroll
-    for (int j = 0; j < NIB; ++j)
-      S.vb_m[j] = col < n && cin ? (uint32_t)s_krow(j) * S.ldb_bm + (uint32_t)col * 2 : OOB;
+    S.vb_m[0] = col < n && cin ? (uint32_t)s_krow(0) * S.ldb_bm + (uint32_t)col * 2 : OOB;
+    S.xb_m = (uint32_t)(2 * SNW) * S.ldb_bm;
     S.db_l = make_desc(L.a_dn + (int64_t)e * n * ra, (int64_t)n * ra * 2);
 #pragma unroll
     for (int j = 0; j < NIB; ++j) {
@@ -276,9 +278,8 @@ __device__ __forceinline__ void s_setup(const Layer& L, const STile& T, const in
     S.ldb_bm = d * 2;
     const int col = c0 + lcm * 8;
     const bool cin = s_in(T, lcm * 8);
-#pragma unroll
-    for (int j = 0; j < NIB; ++j)
-      S.vb_m[j] = col < d && cin ? (uint32_t)s_krow(j) * S.ldb_bm + (uint32_t)col * 2 : OOB;
+    S.vb_m[0] = col < d && cin ? (uint32_t)s_krow(0) * S.ldb_bm + (uint32_t)col * 2 : OOB;
+    S.xb_m = (uint32_t)(2 * SNW) * S.ldb_bm;
     S.db_l = make_desc(L.a_gu + (int64_t)e * d * ra, (int64_t)d * ra * 2);
 #pragma unroll
     for (int j = 0; j < NIB; ++j) {
@@ -304,22 +305,24 @@ __device__ __forceinline__ void s_issue(const SIssue& S, int step, uint32_t sb, 
 #pragma unroll
     for (int j = 0; j < NIA; ++j)
       if (a_on(j))
-        dma16(S.da_m, S.va_m[j], (uint32_t)k0 * 2u, __builtin_amdgcn_readfirstlane(ma + (wid + j * SNW) * 1024));
+        dma16(S.da_m, SP<KIND>::A_MAIN_AFF ? S.va_m[0] + (uint32_t)j * S.xa_m : S.va_m[j], (uint32_t)k0 * 2u,
+              __builtin_amdgcn_readfirstlane(ma + (wid + j * SNW) * 1024));
 #pragma unroll
     for (int j = 0; j < NIB; ++j)
-      dma16(S.db_m, S.vb_m[j], SP<KIND>::B_MAIN_MN ? (uint32_t)k0 * S.ldb_bm : (uint32_t)k0 * 2u,
+      dma16(S.db_m, SP<KIND>::B_MAIN_AFF ? S.vb_m[0] + (uint32_t)j * S.xb_m : S.vb_m[j],
+            SP<KIND>::B_MAIN_MN ? (uint32_t)k0 * S.ldb_bm : (uint32_t)k0 * 2u,
             __builtin_amdgcn_readfirstlane(mb + (wid + j * SNW) * 1024));
   } else {
     const int k0 = (step - S.smain) * SK;
 #pragma unroll
     for (int j = 0; j < NIA; ++j)
       if (a_on(j))
-        dma16(S.da_l, k0 + s_lck(j) * 8 < rs ? S.va_l[j] : OOB, (uint32_t)k0 * 2u,
+        dma16(S.da_l, k0 + s_lck(0) * 8 < rs ? S.va_l[0] + (uint32_t)j * S.xa_l : OOB, (uint32_t)k0 * 2u,
               __builtin_amdgcn_readfirstlane(ma + (wid + j * SNW) * 1024));
 #pragma unroll
     for (int j = 0; j < NIB; ++j) {
       if constexpr (SP<KIND>::B_LORA_MN)
-        dma16(S.db_l, k0 + s_krow(j) < r ? S.vb_l[j] : OOB, (uint32_t)k0 * S.ldb_bl,
+        dma16(S.db_l, k0 + s_krow(j) < r ? S.vb_l[0] + (uint32_t)j * S.xb_l : OOB, (uint32_t)k0 * S.ldb_bl,
               __builtin_amdgcn_readfirstlane(mb + (wid + j * SNW) * 1024));
       else
         dma16(S.db_l, k0 + s_lck(j) * 8 < rs ? S.vb_l[j] : OOB, (uint32_t)k0 * 2u,
@@ -788,13 +791,10 @@ static hipError_t launch_stream(const Layer& L, hipStream_t st, const char* name
   return hipGetLastError();
 }
 
-#if MOE_SK == 32
 hipError_t stream_gate_up(const Layer& L, hipStream_t st) { return launch_stream<SK_GU>(L, st, "gate_up"); }
-#else
 hipError_t stream_down(const Layer& L, hipStream_t st) { return launch_stream<SK_DN>(L, st, "down"); }
 hipError_t stream_dx(const Layer& L, hipStream_t st) { return launch_stream<SK_DX>(L, st, "dx"); }
 hipError_t stream_dh(const Layer& L, hipStream_t st) { return launch_stream<SK_DH>(L, st, "dh"); }
-#endif
 
 }  // inline namespace MOE_EL
 }  // namespace moe
