@@ -50,3 +50,13 @@ def test_more_than_one_gpu_is_refused():
                          capture_output=True, text=True, timeout=120)
     assert res.returncode == 2
     assert "one GPU" in res.stderr
+
+
+def test_hip_flags_keep_packed_fp32_off():
+    """Every HIP object is compiled with the packed-fp32 instructions turned
+    off (the compiler would otherwise form them from plain float code)."""
+    from mixture_experts_lora_amd import build
+    flags = build.HIPCC_FLAGS
+    i = flags.index("-packed-fp32-ops")
+    assert flags[i - 3:i + 1] == ["-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]
+    assert "--offload-arch=gfx950" in flags
