@@ -60,7 +60,9 @@ def kernel_work(c):
     G, H, R, O = P * 2 * n * b, P * n * b, P * r * b, P * d * b
     idx = P * 4 * 2
     logits = c.T * c.E * 4
-    route_out = c.T * c.k * 4 * 2 + c.E * 4 + (c.E + 1) * 4 + P * 4 * 2
+    # ids and weights, counts, offsets, the permutation and its inverse, and
+    # the gather table (token and weight of every sorted row)
+    route_out = c.T * c.k * 4 * 2 + c.E * 4 + (c.E + 1) * 4 + c.T * c.k * 4 * 2 + P * 4 * 2
     work = {
         "route": (0, logits + route_out),
         "prepass_xa": (2 * P * d * r, X + A_gu + R + idx),
@@ -282,7 +284,7 @@ def main():
 
     # routing (all its launches) and the two combines against the HBM peak
     mem = {}
-    route_us = sum(avg_us.get(k, 0.0) for k in ("route_topk_hist", "route_scan_blocks", "route_permute"))
+    route_us = sum(avg_us.get(k, 0.0) for k in ("route_select", "route_scatter"))
     if route_us > 0:
         mem["route"] = {"us": round(route_us, 2), "GB/s": round(work["route"][1] / route_us / 1e3, 1)}
     for k in ("combine_y", "combine_dx"):

@@ -44,8 +44,12 @@
  *  - The return code covers host-side validation and launch errors only; on
  *    any error nothing has been enqueued except in the MOE_ERROR_LAUNCH case.
  *  - Device-side data errors (an expert id outside [0, E) in a routing
- *    struct that did not come from moe_route, non-finite logits) are not
- *    detected; results are then undefined.
+ *    struct that did not come from moe_route) are not detected; results are
+ *    then undefined.
+ *  - Non-finite logits never produce an invalid id: NaN ranks below every
+ *    other value (-inf included) and equal NaNs go to the lower id, like any
+ *    other tie.  The routing weights of a token are defined only when its k
+ *    selected logits are finite (otherwise they may be NaN).
  */
 #ifndef MOE_LORA_H
 #define MOE_LORA_H
@@ -64,8 +68,12 @@ typedef enum {
   MOE_ERROR_INVALID_VALUE = 1, /* null/misaligned pointer, T < 1, k not in [1,E], r < 1,
                                   n_shared not in {0,1}, d or n < 1, non-finite lora_scale */
   MOE_ERROR_UNSUPPORTED = 2,   /* outside the kernel envelope: d or n not a multiple of 64,
-                                  E > 256, r > 128, T*k + n_shared*T >= 2^31,
-                                  T*d*2 or 2n*d*2 bytes >= 2^31 */
+                                  E > 256, r > 128, P_tot = T*k + n_shared*T >= 2^31,
+                                  or any buffer the kernels address with 32-bit byte
+                                  offsets reaching 2^31 bytes: [T, d] and [P_tot, d],
+                                  [P_tot, 2n], [P_tot, n] 16-bit activations, one expert's
+                                  [2n, d] weight, the [P_tot, r] rank-r rows and their
+                                  fp32 partial sums, the [P_tot, n/64] router partials */
   MOE_ERROR_WORKSPACE = 3,     /* a workspace / saved buffer smaller than its size query */
   MOE_ERROR_LAUNCH = 4         /* the HIP runtime reported an error when enqueueing */
 } moe_status;
@@ -96,7 +104,12 @@ typedef struct {
  *   sorted_pair int32 [P]     flat pair index t*k + j at sorted position p;
  *                             expert e owns positions [offsets[e], offsets[e+1]),
  *                             ascending in t (stable)
- *   pair_pos    int32 [P]     inverse permutation: sorted position of pair i */
+ *   pair_pos    int32 [P]     inverse permutation: sorted position of pair i
+ *   row_token   int32 [P_tot] gather table of the sorted rows: the token of
+ *                             row p (sorted_pair[p] / k), and t for the shared
+ *                             expert's row P + t
+ *   row_weight  fp32  [P_tot] routing weight of row p (topk_w of sorted_pair[p]),
+ *                             1 for the shared expert's rows */
 typedef struct {
   int32_t* topk_ids;
   float* topk_w;
@@ -104,6 +117,8 @@ typedef struct {
   int32_t* offsets;
   int32_t* sorted_pair;
   int32_t* pair_pos;
+  int32_t* row_token;
+  float* row_weight;
 } moe_routing;
 
 /* Frozen base weights and LoRA factors, bf16, stacked over E_tot experts:
@@ -128,16 +143,16 @@ const char* moe_status_string(moe_status s);
 /* Size queries.  Each returns 0 if dims is NULL or invalid. */
 size_t moe_route_workspace_bytes(const moe_dims* dims);
 /* Buffer forward fills and backward reads: G [P_tot,2n], H [P_tot,n],
- * X A_gu and H A_dn [P_tot, r] (all bf16), and the token index and routing
- * weight of every sorted row. */
+ * s X A_gu and s H A_dn [P_tot, r] (16-bit). */
 size_t moe_forward_saved_bytes(const moe_dims* dims);
 /* Scratch for one forward or backward call (contents are not preserved). */
 size_t moe_workspace_bytes(const moe_dims* dims);
 
 /* Top-k softmax routing and the one-pass grouping (article section
- * "Optimisation 3: MoE routing grouped once").
- *   logits  fp32 [T, E] router logits (finite)
- *   out     routing buffers to fill (all six pointers required)
+ * "Optimisation 3: MoE routing grouped once"), including the gather table of
+ * the sorted rows (with the shared expert's rows when dims->n_shared is 1).
+ *   logits  fp32 [T, E] router logits
+ *   out     routing buffers to fill (all eight pointers required)
  *   ws      device scratch of at least moe_route_workspace_bytes(dims) */
 moe_status moe_route(const moe_dims* dims, const float* logits, const moe_routing* out,
                      void* ws, size_t ws_bytes, void* stream);

@@ -42,7 +42,8 @@ class MoeDims(ctypes.Structure):
 
 class MoeRouting(ctypes.Structure):
     _fields_ = [(name, ctypes.c_void_p) for name in
-                ("topk_ids", "topk_w", "counts", "offsets", "sorted_pair", "pair_pos")]
+                ("topk_ids", "topk_w", "counts", "offsets", "sorted_pair", "pair_pos",
+                 "row_token", "row_weight")]
 
 
 class MoeWeights(ctypes.Structure):

@@ -3,6 +3,7 @@ marshalling only.  Every step of routing, forward and backward runs in the
 HIP kernels of ``libmoe_lora.so``; nothing here computes."""
 from __future__ import annotations
 
+import contextlib
 import ctypes
 from dataclasses import dataclass
 from typing import NamedTuple, Optional
@@ -59,6 +60,8 @@ class Routing(NamedTuple):
     offsets: torch.Tensor      # int32 [E+1]
     sorted_pair: torch.Tensor  # int32 [P]
     pair_pos: torch.Tensor     # int32 [P]
+    row_token: torch.Tensor    # int32 [P_tot] token of each sorted row
+    row_weight: torch.Tensor   # fp32  [P_tot] routing weight of each sorted row
 
 
 class Weights(NamedTuple):
@@ -102,9 +105,22 @@ def _check(t: torch.Tensor, shape, dtype, name: str) -> None:
         raise ValueError(f"{name}: must be contiguous")
 
 
-def _stream(stream) -> int:
-    s = torch.cuda.current_stream() if stream is None else stream
-    return s.cuda_stream
+@contextlib.contextmanager
+def _on(stream):
+    """Allocations and the library call of one wrapper, on ``stream`` (None =
+    the current stream).  A stream other than the current one first waits for
+    the current stream, where the inputs were produced; tensors allocated
+    inside belong to that stream's pool, so the caching allocator does not hand
+    their memory to other work while the enqueued kernels may still use it.
+    Outputs allocated here are ready on ``stream``; a caller that reads them on
+    another stream orders it after ``stream`` itself."""
+    cur = torch.cuda.current_stream()
+    if stream is None or stream == cur:
+        yield cur.cuda_stream
+        return
+    stream.wait_stream(cur)
+    with torch.cuda.stream(stream):
+        yield stream.cuda_stream
 
 
 def route_workspace_bytes(dims: Dims) -> int:
@@ -133,7 +149,9 @@ def empty_routing(dims: Dims, device) -> Routing:
                    torch.empty(dims.E, dtype=i32, device=device),
                    torch.empty(dims.E + 1, dtype=i32, device=device),
                    torch.empty(dims.P, dtype=i32, device=device),
-                   torch.empty(dims.P, dtype=i32, device=device))
+                   torch.empty(dims.P, dtype=i32, device=device),
+                   torch.empty(dims.P_tot, dtype=i32, device=device),
+                   torch.empty(dims.P_tot, dtype=torch.float32, device=device))
 
 
 def _c_routing(rt: Routing) -> _lib.MoeRouting:
@@ -152,6 +170,8 @@ def _check_routing(rt: Routing, dims: Dims) -> None:
     _check(rt.offsets, (dims.E + 1,), i32, "offsets")
     _check(rt.sorted_pair, (dims.P,), i32, "sorted_pair")
     _check(rt.pair_pos, (dims.P,), i32, "pair_pos")
+    _check(rt.row_token, (dims.P_tot,), i32, "row_token")
+    _check(rt.row_weight, (dims.P_tot,), torch.float32, "row_weight")
 
 
 def _check_weights(w: Weights, dims: Dims) -> None:
@@ -169,13 +189,14 @@ def route(logits: torch.Tensor, dims: Dims, out: Optional[Routing] = None,
     """moe_route: top-k softmax routing and the one-pass grouping."""
     lib = _lib.load()
     _check(logits, (dims.T, dims.E), torch.float32, "logits")
-    out = out if out is not None else empty_routing(dims, logits.device)
-    _check_routing(out, dims)
-    if ws is None:
-        ws = _bytes(route_workspace_bytes(dims), logits.device)
-    dc, rc = dims.c(), _c_routing(out)
-    _lib.check(lib.moe_route(ctypes.byref(dc), logits.data_ptr(), ctypes.byref(rc), ws.data_ptr(),
-                             ws.numel(), _stream(stream)), "moe_route")
+    with _on(stream) as s:
+        out = out if out is not None else empty_routing(dims, logits.device)
+        _check_routing(out, dims)
+        if ws is None:
+            ws = _bytes(route_workspace_bytes(dims), logits.device)
+        dc, rc = dims.c(), _c_routing(out)
+        _lib.check(lib.moe_route(ctypes.byref(dc), logits.data_ptr(), ctypes.byref(rc), ws.data_ptr(),
+                                 ws.numel(), s), "moe_route")
     return out
 
 
@@ -187,17 +208,18 @@ def forward(x: torch.Tensor, routing: Routing, weights: Weights, dims: Dims,
     _check(x, (dims.T, dims.d), dims.elem, "x")
     _check_routing(routing, dims)
     _check_weights(weights, dims)
-    y = y if y is not None else torch.empty_like(x)
-    _check(y, (dims.T, dims.d), dims.elem, "y")
-    if saved is None:
-        saved = _bytes(forward_saved_bytes(dims), x.device)
-    if ws is None:
-        ws = _bytes(workspace_bytes(dims), x.device)
-    dc, rc, wc = dims.c(), _c_routing(routing), _c_weights(weights)
-    _lib.check(lib.moe_lora_forward(ctypes.byref(dc), x.data_ptr(), ctypes.byref(rc),
-                                    ctypes.byref(wc), y.data_ptr(), saved.data_ptr(),
-                                    saved.numel(), ws.data_ptr(), ws.numel(), _stream(stream)),
-               "moe_lora_forward")
+    with _on(stream) as s:
+        y = y if y is not None else torch.empty_like(x)
+        _check(y, (dims.T, dims.d), dims.elem, "y")
+        if saved is None:
+            saved = _bytes(forward_saved_bytes(dims), x.device)
+        if ws is None:
+            ws = _bytes(workspace_bytes(dims), x.device)
+        dc, rc, wc = dims.c(), _c_routing(routing), _c_weights(weights)
+        _lib.check(lib.moe_lora_forward(ctypes.byref(dc), x.data_ptr(), ctypes.byref(rc),
+                                        ctypes.byref(wc), y.data_ptr(), saved.data_ptr(),
+                                        saved.numel(), ws.data_ptr(), ws.numel(), s),
+                   "moe_lora_forward")
     return y, saved
 
 
@@ -226,28 +248,29 @@ def backward(dy: torch.Tensor, x: torch.Tensor, routing: Routing, weights: Weigh
     _check(x, (dims.T, dims.d), dims.elem, "x")
     _check_routing(routing, dims)
     _check_weights(weights, dims)
-    out = out if out is not None else empty_grads(dims, dy.device)
     Et, d, n, r = dims.E_tot, dims.d, dims.n, dims.r
-    _check(out.dx, (dims.T, d), dims.elem, "dx")
-    _check(out.da_gate_up, (Et, d, r), torch.float32, "da_gate_up")
-    _check(out.db_gate_up, (Et, r, 2 * n), torch.float32, "db_gate_up")
-    _check(out.da_down, (Et, n, r), torch.float32, "da_down")
-    _check(out.db_down, (Et, r, d), torch.float32, "db_down")
     dtw = dlg = None
     if router_out is not None:
         _check(router_out.d_topk_w, (dims.T, dims.k), torch.float32, "d_topk_w")
         _check(router_out.d_logits, (dims.T, dims.E), torch.float32, "d_logits")
         dtw, dlg = router_out.d_topk_w.data_ptr(), router_out.d_logits.data_ptr()
-    if ws is None:
-        ws = _bytes(workspace_bytes(dims), dy.device)
-    dc, rc, wc = dims.c(), _c_routing(routing), _c_weights(weights)
-    _lib.check(lib.moe_lora_backward(ctypes.byref(dc), dy.data_ptr(), x.data_ptr(),
-                                     ctypes.byref(rc), ctypes.byref(wc), saved.data_ptr(),
-                                     saved.numel(), out.dx.data_ptr(), out.da_gate_up.data_ptr(),
-                                     out.db_gate_up.data_ptr(), out.da_down.data_ptr(),
-                                     out.db_down.data_ptr(), dtw, dlg, ws.data_ptr(), ws.numel(),
-                                     _stream(stream)),
-               "moe_lora_backward")
+    with _on(stream) as s:
+        out = out if out is not None else empty_grads(dims, dy.device)
+        _check(out.dx, (dims.T, d), dims.elem, "dx")
+        _check(out.da_gate_up, (Et, d, r), torch.float32, "da_gate_up")
+        _check(out.db_gate_up, (Et, r, 2 * n), torch.float32, "db_gate_up")
+        _check(out.da_down, (Et, n, r), torch.float32, "da_down")
+        _check(out.db_down, (Et, r, d), torch.float32, "db_down")
+        if ws is None:
+            ws = _bytes(workspace_bytes(dims), dy.device)
+        dc, rc, wc = dims.c(), _c_routing(routing), _c_weights(weights)
+        _lib.check(lib.moe_lora_backward(ctypes.byref(dc), dy.data_ptr(), x.data_ptr(),
+                                         ctypes.byref(rc), ctypes.byref(wc), saved.data_ptr(),
+                                         saved.numel(), out.dx.data_ptr(), out.da_gate_up.data_ptr(),
+                                         out.db_gate_up.data_ptr(), out.da_down.data_ptr(),
+                                         out.db_down.data_ptr(), dtw, dlg, ws.data_ptr(), ws.numel(),
+                                         s),
+                   "moe_lora_backward")
     return out
 
 
@@ -278,11 +301,12 @@ def autotune(dims: Dims, logits: torch.Tensor, x: torch.Tensor, dy: torch.Tensor
     _check(dy, (dims.T, dims.d), dims.elem, "dy")
     _check_weights(weights, dims)
     dc, wc = dims.c(), _c_weights(weights)
-    scratch = _bytes(int(lib.moe_autotune_scratch_bytes(ctypes.byref(dc))), x.device)
     out = ctypes.c_uint(0)
-    _lib.check(lib.moe_autotune(ctypes.byref(dc), logits.data_ptr(), x.data_ptr(), dy.data_ptr(),
-                                ctypes.byref(wc), scratch.data_ptr(), scratch.numel(),
-                                _stream(stream), ctypes.byref(out)), "moe_autotune")
+    with _on(stream) as s:
+        scratch = _bytes(int(lib.moe_autotune_scratch_bytes(ctypes.byref(dc))), x.device)
+        _lib.check(lib.moe_autotune(ctypes.byref(dc), logits.data_ptr(), x.data_ptr(), dy.data_ptr(),
+                                    ctypes.byref(wc), scratch.data_ptr(), scratch.numel(),
+                                    s, ctypes.byref(out)), "moe_autotune")
     return int(out.value)
 
 

@@ -21,10 +21,16 @@ moe_status check_dims(const moe_dims* dm) {
   if (dm->d % 64 || dm->n % 64 || dm->E > 256 || dm->r > 128) return MOE_ERROR_UNSUPPORTED;
   const int64_t ptot = dm->T * (int64_t)dm->k + (int64_t)dm->n_shared * dm->T;
   if (ptot >= ((int64_t)1 << 31)) return MOE_ERROR_UNSUPPORTED;
-  // 32-bit buffer offsets: a [T, d] activation and one expert's [2n, d] weight
-  // must each stay below 2 GiB
-  if (dm->T * (int64_t)dm->d * 2 >= ((int64_t)1 << 31)) return MOE_ERROR_UNSUPPORTED;
-  if ((int64_t)2 * dm->n * dm->d * 2 >= ((int64_t)1 << 31)) return MOE_ERROR_UNSUPPORTED;
+  // Buffer resources take 32-bit byte offsets below 2^31 (0x80000000 is the
+  // out-of-range marker), so every buffer the kernels address that way must
+  // stay below 2 GiB: the widest per-row buffers are [P_tot, max(2n, d)]
+  // 16-bit (O, dX per pair, G, dG); H, the rank-r rows (r <= 128 < 2n), the
+  // per-row tables and the router partials are narrower per row, and [T, d]
+  // has fewer rows.  One expert's [2n, d] weight is addressed the same way.
+  const int64_t lim = (int64_t)1 << 31;
+  const int64_t widest = 2 * (int64_t)(2 * dm->n > dm->d ? 2 * dm->n : dm->d);
+  if (ptot * widest >= lim) return MOE_ERROR_UNSUPPORTED;
+  if ((int64_t)2 * dm->n * dm->d * 2 >= lim) return MOE_ERROR_UNSUPPORTED;
   return MOE_SUCCESS;
 }
 
@@ -51,8 +57,9 @@ Layer make_layer(const moe_dims* dm) {
 
 moe_status check_routing_in(const moe_routing* rt) {
   if (!rt) return MOE_ERROR_INVALID_VALUE;
-  if (!aligned16(rt->topk_w) || !aligned16(rt->offsets) || !aligned16(rt->sorted_pair) ||
-      !aligned16(rt->pair_pos))
+  if (!aligned16(rt->topk_ids) || !aligned16(rt->topk_w) || !aligned16(rt->offsets) ||
+      !aligned16(rt->sorted_pair) || !aligned16(rt->pair_pos) || !aligned16(rt->row_token) ||
+      !aligned16(rt->row_weight))
     return MOE_ERROR_INVALID_VALUE;
   return MOE_SUCCESS;
 }
@@ -77,6 +84,8 @@ void attach_common(Layer& L, const moe_routing* rt, const moe_weights* w, const 
   L.offsets = rt->offsets;
   L.sorted_pair = rt->sorted_pair;
   L.pair_pos = rt->pair_pos;
+  L.tok = rt->row_token;
+  L.wgt = rt->row_weight;
   L.w_gu = w->w_gate_up;
   L.w_dn = w->w_down;
   L.b_gu = w->b_gate_up;
@@ -110,8 +119,6 @@ void attach_saved(Layer& L, const moe_dims* dm, void* saved) {
   L.h = (bf16_t*)(base + sl.h);
   L.xa = (bf16_t*)(base + sl.xa);
   L.ha = (bf16_t*)(base + sl.ha);
-  L.tok = (const int32_t*)(base + sl.tok);
-  L.wgt = (const float*)(base + sl.wgt);
 }
 
 hipError_t maybe_pack(const Layer& L, const moe_weights* w, hipStream_t st) {
@@ -153,14 +160,13 @@ moe_status moe_route(const moe_dims* dm, const float* logits, const moe_routing*
                      size_t ws_bytes, void* stream) {
   moe_status st = check_dims(dm);
   if (st != MOE_SUCCESS) return st;
-  if (!aligned16(logits) || !out || !aligned16(out->topk_ids) || !aligned16(out->topk_w) ||
-      !aligned16(out->counts) || !aligned16(out->offsets) || !aligned16(out->sorted_pair) ||
-      !aligned16(out->pair_pos) || !aligned16(ws))
+  if (!aligned16(logits) || !out || !aligned16(out->counts) || check_routing_in(out) != MOE_SUCCESS ||
+      !aligned16(ws))
     return MOE_ERROR_INVALID_VALUE;
   if (ws_bytes < route_ws_bytes(dm->T, dm->E, dm->k)) return MOE_ERROR_WORKSPACE;
-  return launched(launch_route(logits, dm->T, dm->E, dm->k, out->topk_ids, out->topk_w,
-                               out->counts, out->offsets, out->sorted_pair, out->pair_pos, ws,
-                               (hipStream_t)stream));
+  return launched(launch_route(logits, dm->T, dm->E, dm->k, dm->n_shared, out->topk_ids, out->topk_w,
+                               out->counts, out->offsets, out->sorted_pair, out->pair_pos,
+                               out->row_token, out->row_weight, ws, (hipStream_t)stream));
 }
 
 moe_status moe_lora_forward(const moe_dims* dm, const moe_bf16* x, const moe_routing* rt,
@@ -181,7 +187,6 @@ moe_status moe_lora_forward(const moe_dims* dm, const moe_bf16* x, const moe_rou
   L.x = x;
   L.y = y;
   hipError_t e = maybe_pack(L, w, s);
-  if (e == hipSuccess) e = launch_gather_table(L, (int32_t*)L.tok, (float*)L.wgt, s);
   if (e == hipSuccess) e = EL(L, gemm_gate_up, L, s);
   if (e == hipSuccess) e = EL(L, gemm_down, L, s);
   if (e == hipSuccess) e = EL(L, launch_combine, L, true, L.o, L.y, s);

@@ -78,7 +78,7 @@ struct Layer {
   float* partial;    // split-K partial sums of the LoRA gradients
   float* pre_partial;  // split-K partial sums of the rank-r pre-passes [split][Ptot][rs]
   int64_t partial_off[4];  // float offset of each gradient's partial slots
-  const int32_t* tok;      // [Ptot] token of each sorted row (gather table)
+  const int32_t* tok;      // [Ptot] token of each sorted row (routing's gather table)
   const float* wgt;        // [Ptot] routing weight of each sorted row (1 for shared)
 };
 
@@ -95,15 +95,15 @@ struct WsLayout {
   int64_t partial_off[4];
 };
 struct SavedLayout {
-  size_t g, h, xa, ha, tok, wgt, total;
+  size_t g, h, xa, ha, total;
 };
 WsLayout ws_layout(int64_t T, int d, int n, int E, int k, int r, int S);
 SavedLayout saved_layout(int64_t T, int d, int n, int E, int k, int r, int S);
 
 size_t route_ws_bytes(int64_t T, int E, int k);
-hipError_t launch_route(const float* logits, int64_t T, int E, int k, int32_t* ids, float* w,
-                        int32_t* counts, int32_t* offsets, int32_t* sorted_pair,
-                        int32_t* pair_pos, void* ws, hipStream_t st);
+hipError_t launch_route(const float* logits, int64_t T, int E, int k, int S, int32_t* ids, float* w,
+                        int32_t* counts, int32_t* offsets, int32_t* sorted_pair, int32_t* pair_pos,
+                        int32_t* row_token, float* row_weight, void* ws, hipStream_t st);
 
 // Rank-r pre-pass kinds: s X A_gu, s H A_dn, s dY B_dn^T, s dG B_gu^T.
 enum PrepassKind { PRE_XA = 0, PRE_HA = 1, PRE_QDN = 2, PRE_QGU = 3 };
@@ -147,11 +147,9 @@ MOE_ELEMENT_LAUNCHERS
 }
 #endif
 
-// Element-wise / gather kernels that do not depend on the element type
-// (layer.hip).
+// Kernels that do not depend on the element type (layer.hip).
 hipError_t launch_pack_a(const Layer& L, const bf16_t* a_gu_src, const bf16_t* a_dn_src,
                          bf16_t* a_gu_dst, bf16_t* a_dn_dst, hipStream_t st);
-hipError_t launch_gather_table(const Layer& L, int32_t* tok, float* wgt, hipStream_t st);
 // Routing-weight and logit gradients from the dh epilogue's partials.
 hipError_t launch_router_grad(const Layer& L, float* d_topk_w, float* d_logits, hipStream_t st);
 // Shape -> engines table (tune.hip): a recorded choice, else default_engines().

@@ -1,4 +1,4 @@
-// Gather table, LoRA-factor packing, router gradients and buffer layouts
+// LoRA-factor packing, router gradients and buffer layouts
 // (nothing here depends on the element type).
 #include <atomic>
 
@@ -52,8 +52,6 @@ SavedLayout saved_layout(int64_t T, int d, int n, int E, int k, int r, int S) {
   s.h = off;  off += align256((size_t)Ptot * n * 2);
   s.xa = off; off += align256((size_t)Ptot * rs * 2);
   s.ha = off; off += align256((size_t)Ptot * rs * 2);
-  s.tok = off; off += align256((size_t)Ptot * 4);
-  s.wgt = off; off += align256((size_t)Ptot * 4);
   s.total = off;
   return s;
 }
@@ -93,28 +91,6 @@ hipError_t launch_pack_a(const Layer& L, const bf16_t* a_gu_src, const bf16_t* a
   const int gd = (int)std::min<int64_t>(cdiv64(rows_dn * L.rs, 256), 4096);
   MOE_LAUNCH("pack_a", k_pack_rank, dim3(gb), dim3(256), 0, st, a_gu_src, a_gu_dst, rows_gu, L.r, L.rs);
   MOE_LAUNCH("pack_a", k_pack_rank, dim3(gd), dim3(256), 0, st, a_dn_src, a_dn_dst, rows_dn, L.r, L.rs);
-  return hipGetLastError();
-}
-
-// Gather table of the sorted rows: token index and routing weight (the
-// shared expert's rows p >= P are token p - P with weight 1).
-__global__ __launch_bounds__(256) void k_gather_table(const Layer L, int32_t* __restrict__ tok,
-                                                      float* __restrict__ wgt) {
-  for (int p = blockIdx.x * 256 + threadIdx.x; p < L.Ptot; p += gridDim.x * 256) {
-    if (p < L.P) {
-      const int i = L.sorted_pair[p];
-      tok[p] = i / L.k;
-      wgt[p] = L.topk_w[i];
-    } else {
-      tok[p] = p - L.P;
-      wgt[p] = 1.0f;
-    }
-  }
-}
-
-hipError_t launch_gather_table(const Layer& L, int32_t* tok, float* wgt, hipStream_t st) {
-  const int g = std::min(cdiv(L.Ptot, 256), 2048);
-  MOE_LAUNCH("gather_table", k_gather_table, dim3(g), dim3(256), 0, st, L, tok, wgt);
   return hipGetLastError();
 }
 

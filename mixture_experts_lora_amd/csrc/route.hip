@@ -1,203 +1,272 @@
 // Routing: top-k softmax and the one-pass grouping of (token, slot) pairs by
 // expert (article on Unsloth x NVIDIA training optimisations, section
 // "Optimisation 3: MoE routing grouped once": flatten, stable sort by expert
-// id, one bincount, offsets from counts, slice by offset).
+// id, one bincount, offsets from counts, slice by offset, gather).
 //
-// Three kernels, no host round trip:
-//   1. route_topk_hist  one workgroup per block of 16 tokens (16 lanes per
-//      token, logits in registers): top-k + softmax, then an LDS-private
-//      per-expert token bitmask (16 bits = the block's tokens).  Popcounts of the bitmask give the block's histogram row and
-//      every pair's rank among the block's earlier pairs of the same expert
-//      (a token never picks an expert twice, so rank within the block equals
-//      the number of earlier tokens that picked it: the sort stays stable
-//      without atomics deciding any order).
-//   2. route_scan_blocks  one workgroup per expert: exclusive scan of that
-//      expert's histogram column over blocks (-> block bases) and its total
-//      (-> counts, the bincount).
-//   3. route_permute  exclusive scan of counts (-> offsets, E+1 entries), then
-//      dest = offsets[e] + base[block][e] + rank; sorted_pair[dest] = i and
-//      pair_pos[i] = dest.
+// Two kernels, no host round trip:
+//   1. route_select  at most 256 workgroups, each a contiguous block of
+//      tokens taken 16 at a time; a token is one 16-lane DPP row.  Its
+//      logits become 64-bit keys (order-preserving bits of the value, then
+//      the complement of the expert id), so "largest logit, ties to the
+//      lower id" is one unsigned maximum; pick j is the row maximum of the
+//      keys below pick j-1, reduced over the row with DPP rotations.  Softmax
+//      over the picks.  An LDS-private per-expert token bitmask (16 bits per
+//      round of 16 tokens) gives, by popcount, every pair's rank among the
+//      block's earlier pairs of its expert (a token never picks an expert
+//      twice, so that rank is the number of earlier tokens that picked it:
+//      the sort stays stable without atomics deciding any order) and the
+//      block's histogram row.
+//   2. route_scatter  at most 64 workgroups of 1024 threads.  Each sums the
+//      histogram columns (the bincount: totals, and the part below its own
+//      range of blocks), scans the totals into the exclusive offsets, then
+//      places every pair of its range: dest = offsets[e] + (pairs of e in
+//      earlier blocks) + rank.  It writes sorted_pair, its inverse pair_pos,
+//      and the gather table of the sorted rows (token and routing weight of
+//      each row; the shared expert's rows P + t are token t with weight 1).
 #include "common.h"
+#include "gemm_util.h"
 #include "kernels.h"
 
 namespace moe {
 
-constexpr int RT_TOK = 16;      // tokens per routing block
-constexpr int RT_LANES = 16;    // lanes per token; each holds up to 16 logits
-constexpr int RT_THREADS = RT_TOK * RT_LANES;
-constexpr int SCAN_THREADS = 256;
-constexpr int PERM_BLOCKS = 4;  // routing blocks per permute workgroup
-constexpr int PERM_THREADS = 256;
+constexpr int RS_TOK = 16;              // tokens per round of route_select (one 16-lane row each)
+constexpr int RS_THREADS = RS_TOK * 16;
+constexpr int RS_MAXBLK = 256;          // route_select workgroups at most
+constexpr int SC_THREADS = 1024;        // route_scatter workgroup
+constexpr int SC_MAXBLK = 64;           // route_scatter workgroups at most
 
-// (v, e) comes strictly before (bv, be) in the order value descending, id
-// ascending; be < 0 marks "nothing yet"
-__device__ __forceinline__ bool rt_before(float v, int e, float bv, int be) {
-  return be < 0 || v > bv || (v == bv && e < be);
+struct RouteGeom {
+  int spb;    // rounds of 16 tokens per route_select workgroup
+  int nblk;   // route_select workgroups (histogram rows)
+  int bpb2;   // histogram rows per route_scatter workgroup
+  int nblk2;  // route_scatter workgroups
+};
+
+static RouteGeom route_geom(int64_t T) {
+  RouteGeom g;
+  const int nsub = (int)cdiv64(T, RS_TOK);
+  const int nb = nsub < RS_MAXBLK ? nsub : RS_MAXBLK;
+  g.spb = cdiv(nsub, nb);
+  g.nblk = cdiv(nsub, g.spb);
+  g.bpb2 = cdiv(g.nblk, SC_MAXBLK);
+  g.nblk2 = cdiv(g.nblk, g.bpb2);
+  return g;
 }
 
-// One workgroup per block of 16 tokens, 16 lanes per token.  A lane keeps its
-// token's logits e = lane, lane+16, ... in registers; pick j is the best
-// element strictly after pick j-1, found by a register scan and a 16-lane
-// shuffle reduction.  The picks go to LDS, then the softmax weights, the
-// block's per-expert token bitmask (16 bits), the in-block ranks and the
-// histogram row follow from there.
-__global__ __launch_bounds__(RT_THREADS) void route_topk_hist(
-    const float* __restrict__ logits, int T, int E, int k, int32_t* __restrict__ topk_ids,
-    float* __restrict__ topk_w, int32_t* __restrict__ blk_counts, int32_t* __restrict__ local_rank) {
-  extern __shared__ unsigned char rt_smem[];
-  int* sel_id = (int*)rt_smem;                    // [RT_TOK][k]
-  float* sel_v = (float*)(sel_id + RT_TOK * k);  // [RT_TOK][k]
-  __shared__ uint32_t mask[256];
-  const int b = blockIdx.x;
-  const int t0 = b * RT_TOK;
-  const int ntok = min(RT_TOK, T - t0);
-  const int tl = threadIdx.x / RT_LANES;
-  const int sub = threadIdx.x % RT_LANES;
-  const bool valid = tl < ntok;
-  const int t = t0 + tl;
-  for (int i = threadIdx.x; i < E; i += RT_THREADS) mask[i] = 0u;
+// Order-preserving unsigned image of a logit: larger value -> larger image,
+// -0 and +0 equal, NaN below every other value (-inf included).
+__device__ __forceinline__ uint32_t rt_ord(float v) {
+  uint32_t u = __float_as_uint(v);
+  if (v != v) return 0u;
+  if ((u << 1) == 0u) u = 0u;
+  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+// inverse of rt_ord (the NaN image 0 maps back to a NaN)
+__device__ __forceinline__ float rt_val(uint32_t o) {
+  return __uint_as_float((o & 0x80000000u) ? (o & 0x7fffffffu) : ~o);
+}
 
-  float v[16];
-  const float* row = logits + (int64_t)t * E;
-#pragma unroll
-  for (int i = 0; i < 16; ++i) {
-    const int e = sub + RT_LANES * i;
-    v[i] = (valid && e < E) ? row[e] : -INFINITY;
+// DPP row_ror:N (rotate within each 16-lane row) of a 32-bit value
+template <int N>
+__device__ __forceinline__ uint32_t ror_row(uint32_t x) {
+  return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x120 | N, 0xf, 0xf, false);
+}
+template <int N>
+__device__ __forceinline__ uint64_t ror_row64(uint64_t x) {
+  return ((uint64_t)ror_row<N>((uint32_t)(x >> 32)) << 32) | ror_row<N>((uint32_t)x);
+}
+// maximum / sum over the 16 lanes of a row; every lane of the row gets the
+// same result (rotations by 8, 4, 2, 1 pair each lane with lanes whose
+// partial results equal its own, so even the float sum is bitwise the same)
+__device__ __forceinline__ uint64_t row_max64(uint64_t x) {
+  uint64_t y;
+  y = ror_row64<8>(x); x = y > x ? y : x;
+  y = ror_row64<4>(x); x = y > x ? y : x;
+  y = ror_row64<2>(x); x = y > x ? y : x;
+  y = ror_row64<1>(x); x = y > x ? y : x;
+  return x;
+}
+__device__ __forceinline__ float row_sum(float x) {
+  x += __uint_as_float(ror_row<8>(__float_as_uint(x)));
+  x += __uint_as_float(ror_row<4>(__float_as_uint(x)));
+  x += __uint_as_float(ror_row<2>(__float_as_uint(x)));
+  x += __uint_as_float(ror_row<1>(__float_as_uint(x)));
+  return x;
+}
+
+__global__ __launch_bounds__(RS_THREADS) void route_select(
+    const float* __restrict__ logits, int T, int E, int k, int spb, int32_t* __restrict__ topk_ids,
+    float* __restrict__ topk_w, int32_t* __restrict__ blk_counts, int32_t* __restrict__ local_rank) {
+  extern __shared__ __attribute__((aligned(8))) unsigned char rs_smem[];
+  uint64_t* sel = (uint64_t*)rs_smem;  // [RS_TOK][k] picked keys
+  __shared__ uint32_t mask[256];       // tokens of this round that picked expert e
+  __shared__ int cnt[256];             // pairs of expert e in earlier rounds of the block
+  const int tl = threadIdx.x >> 4, sub = threadIdx.x & 15;
+  for (int e = threadIdx.x; e < E; e += RS_THREADS) {
+    mask[e] = 0u;
+    cnt[e] = 0;
   }
-  float pv = INFINITY;
-  int pe = -1;
-  for (int j = 0; j < k; ++j) {
-    float bv = -INFINITY;
-    int be = -1;
+  __syncthreads();
+  const int nv = (E + 15) >> 4;  // keys per lane
+#pragma unroll 1
+  for (int s = 0; s < spb; ++s) {
+    const int64_t t0 = ((int64_t)blockIdx.x * spb + s) * RS_TOK;
+    if (t0 >= T) break;  // uniform over the workgroup
+    const int64_t t = t0 + tl;
+    const bool valid = t < T;
+    // lane sub keeps the keys of experts sub, sub + 16, ...; absent ones are 0
+    uint64_t key[16];
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
-      const int e = sub + RT_LANES * i;
-      const bool after = (v[i] < pv) || (v[i] == pv && e > pe);
-      if (e < E && after && rt_before(v[i], e, bv, be)) {
-        bv = v[i];
-        be = e;
+      const int e = sub + 16 * i;
+      key[i] = 0;
+      if (i < nv && valid && e < E)
+        key[i] = ((uint64_t)rt_ord(logits[t * E + e]) << 32) | (uint64_t)(0xffffffffu - (uint32_t)e);
+    }
+    uint64_t prev = ~(uint64_t)0;
+#pragma unroll 1
+    for (int j = 0; j < k; ++j) {
+      uint64_t best = 0;
+#pragma unroll
+      for (int i = 0; i < 16; ++i)
+        if (i < nv) best = (key[i] < prev && key[i] > best) ? key[i] : best;
+      best = row_max64(best);
+      prev = best;
+      if (sub == (j & 15)) sel[tl * k + j] = best;
+    }
+    __syncthreads();
+    // softmax of the k picked logits, relative to the largest
+    const float v0 = rt_val((uint32_t)(sel[tl * k] >> 32));
+    float part = 0.0f;
+    for (int j = sub; j < k; j += 16) part += expf(rt_val((uint32_t)(sel[tl * k + j] >> 32)) - v0);
+    const float inv = 1.0f / row_sum(part);
+    if (valid) {
+      for (int j = sub; j < k; j += 16) {
+        const uint64_t kk = sel[tl * k + j];
+        const int id = (int)(0xffffffffu - (uint32_t)kk);
+        topk_ids[t * k + j] = id;
+        topk_w[t * k + j] = expf(rt_val((uint32_t)(kk >> 32)) - v0) * inv;
+        atomicOr(&mask[id], 1u << tl);
       }
     }
-#pragma unroll
-    for (int m = 1; m < RT_LANES; m <<= 1) {
-      const float ov = __shfl_xor(bv, m, 64);
-      const int oe = __shfl_xor(be, m, 64);
-      if (oe >= 0 && rt_before(ov, oe, bv, be)) {
-        bv = ov;
-        be = oe;
+    __syncthreads();
+    if (valid) {
+      for (int j = sub; j < k; j += 16) {
+        const int id = (int)(0xffffffffu - (uint32_t)sel[tl * k + j]);
+        local_rank[t * k + j] = cnt[id] + __popc(mask[id] & ((1u << tl) - 1u));
       }
     }
-    pv = bv;
-    pe = be;
-    if (sub == 0) {
-      sel_id[tl * k + j] = be;
-      sel_v[tl * k + j] = bv;
+    __syncthreads();
+    for (int e = threadIdx.x; e < E; e += RS_THREADS) {
+      cnt[e] += __popc(mask[e]);
+      mask[e] = 0u;
     }
+    __syncthreads();
   }
-  __syncthreads();
-  if (valid) {
-    const float v0 = sel_v[tl * k];
-    float sum = 0.0f;
-    for (int j = 0; j < k; ++j) sum += expf(sel_v[tl * k + j] - v0);
-    const float inv = 1.0f / sum;
-    for (int j = sub; j < k; j += RT_LANES) {
-      const int id = sel_id[tl * k + j];
-      topk_ids[(int64_t)t * k + j] = id;
-      topk_w[(int64_t)t * k + j] = expf(sel_v[tl * k + j] - v0) * inv;
-      atomicOr(&mask[id], 1u << tl);
-    }
-  }
-  __syncthreads();
-  if (valid) {
-    for (int j = sub; j < k; j += RT_LANES) {
-      const int id = sel_id[tl * k + j];
-      local_rank[(int64_t)t * k + j] = __popc(mask[id] & ((1u << tl) - 1u));
-    }
-  }
-  for (int e = threadIdx.x; e < E; e += RT_THREADS)
-    blk_counts[(int64_t)b * E + e] = __popc(mask[e]);
+  for (int e = threadIdx.x; e < E; e += RS_THREADS) blk_counts[(int64_t)blockIdx.x * E + e] = cnt[e];
 }
 
-__global__ __launch_bounds__(SCAN_THREADS) void route_scan_blocks(int32_t* __restrict__ blk,
-                                                                  int nblk, int E,
-                                                                  int32_t* __restrict__ counts) {
-  __shared__ int sh[4];
-  const int e = blockIdx.x;
-  const int per = (nblk + SCAN_THREADS - 1) / SCAN_THREADS;
-  const int b0 = threadIdx.x * per, b1 = min(nblk, b0 + per);
-  int s = 0;
-  for (int b = b0; b < b1; ++b) s += blk[(int64_t)b * E + e];
-  int total;
-  int base = block_excl_scan256(s, sh, &total);
-  for (int b = b0; b < b1; ++b) {
-    const int c = blk[(int64_t)b * E + e];
-    blk[(int64_t)b * E + e] = base;
-    base += c;
-  }
-  if (threadIdx.x == 0) counts[e] = total;
-}
-
-__global__ __launch_bounds__(PERM_THREADS) void route_permute(
-    const int32_t* __restrict__ topk_ids, const int32_t* __restrict__ counts,
-    const int32_t* __restrict__ bases, const int32_t* __restrict__ local_rank, int T, int E, int k,
-    int nblk, int32_t* __restrict__ offsets, int32_t* __restrict__ sorted_pair,
-    int32_t* __restrict__ pair_pos) {
-  __shared__ int offs[256 + 1];
-  __shared__ int bb[PERM_BLOCKS][256];
-  __shared__ int sh[4];
-  const int pb = blockIdx.x;
-  const int e = threadIdx.x;
-  const int c = e < E ? counts[e] : 0;
-  int total;
-  const int o = block_excl_scan256(c, sh, &total);
-  if (e < E) {
-    offs[e] = o;
-#pragma unroll
-    for (int q = 0; q < PERM_BLOCKS; ++q) {
-      const int b = pb * PERM_BLOCKS + q;
-      bb[q][e] = b < nblk ? bases[(int64_t)b * E + e] : 0;
+__global__ __launch_bounds__(SC_THREADS) void route_scatter(
+    const int32_t* __restrict__ topk_ids, const float* __restrict__ topk_w,
+    const int32_t* __restrict__ blk_counts, const int32_t* __restrict__ local_rank, int T, int E, int k,
+    int S, int spb, int nblk, int bpb2, int32_t* __restrict__ counts, int32_t* __restrict__ offsets,
+    int32_t* __restrict__ sorted_pair, int32_t* __restrict__ pair_pos, int32_t* __restrict__ row_token,
+    float* __restrict__ row_weight) {
+  __shared__ int part_lo[SC_THREADS];   // [group][expert] histogram rows below this range
+  __shared__ int part_tot[SC_THREADS];  // [group][expert] all histogram rows
+  __shared__ int base[256];             // pairs of expert e before the current block
+  __shared__ int off[256 + 1];
+  __shared__ int sh[SC_THREADS / 64];
+  const int tid = threadIdx.x;
+  const int bfirst = blockIdx.x * bpb2, blast = min(nblk, bfirst + bpb2);
+  // column sums of the histogram, rows split over ng groups of E threads
+  const int ng = SC_THREADS / E;
+  const int g = tid / E, e = tid - g * E;
+  int lo = 0, tot = 0;
+  if (g < ng) {
+    const int ch = cdiv(nblk, ng);
+    const int r0 = g * ch, r1 = min(nblk, r0 + ch);
+#pragma unroll 8
+    for (int rb = r0; rb < r1; ++rb) {
+      const int c = blk_counts[(int64_t)rb * E + e];
+      tot += c;
+      lo += rb < bfirst ? c : 0;
     }
   }
-  if (e == 0) offs[E] = total;
-  if (pb == 0) {
-    if (e < E) offsets[e] = o;
-    if (e == 0) offsets[E] = total;
+  part_lo[tid] = lo;
+  part_tot[tid] = tot;
+  __syncthreads();
+  int c_e = 0;
+  if (tid < E) {
+    int l = 0;
+    for (int gg = 0; gg < ng; ++gg) {
+      l += part_lo[gg * E + tid];
+      c_e += part_tot[gg * E + tid];
+    }
+    base[tid] = l;
+  }
+  int total;
+  const int o = block_excl_scan<SC_THREADS / 64>(c_e, sh, &total);
+  if (tid < E) {
+    off[tid] = o;
+    if (blockIdx.x == 0) {
+      counts[tid] = c_e;
+      offsets[tid] = o;
+    }
+  }
+  if (tid == 0) {
+    off[E] = total;
+    if (blockIdx.x == 0) offsets[E] = total;
   }
   __syncthreads();
-  const int64_t tok0 = (int64_t)pb * PERM_BLOCKS * RT_TOK;
-  const int64_t i0 = tok0 * k;
-  const int64_t i1 = min((int64_t)T, tok0 + PERM_BLOCKS * RT_TOK) * k;
-  for (int64_t i = i0 + threadIdx.x; i < i1; i += PERM_THREADS) {
-    const int id = topk_ids[i];
-    const int q = (int)((i / k - tok0) / RT_TOK);
-    const int dest = offs[id] + bb[q][id] + local_rank[i];
-    sorted_pair[dest] = (int32_t)i;
-    pair_pos[i] = dest;
+  const int64_t tok_per_blk = (int64_t)spb * RS_TOK;
+#pragma unroll 1
+  for (int rb = bfirst; rb < blast; ++rb) {
+    const int64_t i0 = rb * tok_per_blk * k;
+    const int64_t i1 = min((int64_t)T, (rb + 1) * tok_per_blk) * k;
+    for (int64_t i = i0 + tid; i < i1; i += SC_THREADS) {
+      const int id = topk_ids[i];
+      const int dest = off[id] + base[id] + local_rank[i];
+      sorted_pair[dest] = (int32_t)i;
+      pair_pos[i] = dest;
+      row_token[dest] = (int32_t)(i / k);
+      row_weight[dest] = topk_w[i];
+    }
+    __syncthreads();  // every thread has read base before it moves on
+    if (tid < E) base[tid] += blk_counts[(int64_t)rb * E + tid];
+    __syncthreads();
+  }
+  if (S) {
+    const int64_t P = (int64_t)T * k;
+    const int64_t ta = bfirst * tok_per_blk, tb = min((int64_t)T, blast * tok_per_blk);
+    for (int64_t t = ta + tid; t < tb; t += SC_THREADS) {
+      row_token[P + t] = (int32_t)t;
+      row_weight[P + t] = 1.0f;
+    }
   }
 }
 
 size_t route_ws_bytes(int64_t T, int E, int k) {
-  const int64_t nblk = cdiv64(T, RT_TOK);
-  size_t a = (size_t)nblk * E * sizeof(int32_t);
+  const RouteGeom g = route_geom(T);
+  size_t a = (size_t)g.nblk * E * sizeof(int32_t);
   a = (a + 255) & ~(size_t)255;
   return a + (size_t)T * k * sizeof(int32_t);
 }
 
-hipError_t launch_route(const float* logits, int64_t T, int E, int k, int32_t* ids, float* w,
-                        int32_t* counts, int32_t* offsets, int32_t* sorted_pair,
-                        int32_t* pair_pos, void* ws, hipStream_t st) {
-  const int nblk = (int)cdiv64(T, RT_TOK);
-  size_t a = (size_t)nblk * E * sizeof(int32_t);
+hipError_t launch_route(const float* logits, int64_t T, int E, int k, int S, int32_t* ids, float* w,
+                        int32_t* counts, int32_t* offsets, int32_t* sorted_pair, int32_t* pair_pos,
+                        int32_t* row_token, float* row_weight, void* ws, hipStream_t st) {
+  const RouteGeom g = route_geom(T);
+  size_t a = (size_t)g.nblk * E * sizeof(int32_t);
   a = (a + 255) & ~(size_t)255;
   int32_t* blk = (int32_t*)ws;
   int32_t* rank = (int32_t*)((char*)ws + a);
-  const size_t lds = (size_t)RT_TOK * k * (sizeof(int) + sizeof(float));
-  MOE_LAUNCH("route_topk_hist", route_topk_hist, dim3(nblk), dim3(RT_THREADS), lds, st, logits, (int)T, E, k,
-                     ids, w, blk, rank);
-  MOE_LAUNCH("route_scan_blocks", route_scan_blocks, dim3(E), dim3(SCAN_THREADS), 0, st, blk, nblk, E,
-             counts);
-  MOE_LAUNCH("route_permute", route_permute, dim3(cdiv(nblk, PERM_BLOCKS)), dim3(PERM_THREADS), 0, st,
-             ids, counts, blk, rank, (int)T, E, k, nblk, offsets, sorted_pair, pair_pos);
+  const size_t lds = (size_t)RS_TOK * k * sizeof(uint64_t);
+  MOE_LAUNCH("route_select", route_select, dim3(g.nblk), dim3(RS_THREADS), lds, st, logits, (int)T, E, k,
+             g.spb, ids, w, blk, rank);
+  MOE_LAUNCH("route_scatter", route_scatter, dim3(g.nblk2), dim3(SC_THREADS), 0, st, ids, w, blk, rank,
+             (int)T, E, k, S, g.spb, g.nblk, g.bpb2, counts, offsets, sorted_pair, pair_pos, row_token,
+             row_weight);
   return hipGetLastError();
 }
 

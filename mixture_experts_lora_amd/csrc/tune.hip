@@ -64,6 +64,8 @@ TuneBufs carve(const moe_dims* dm, char* base) {
   b.rt.offsets = (int32_t*)take((E + 1) * 4);
   b.rt.sorted_pair = (int32_t*)take(P * 4);
   b.rt.pair_pos = (int32_t*)take(P * 4);
+  b.rt.row_token = (int32_t*)take((P + dm->n_shared * T) * 4);
+  b.rt.row_weight = (float*)take((P + dm->n_shared * T) * 4);
   b.route_ws_bytes = moe_route_workspace_bytes(dm);
   b.saved_bytes = moe_forward_saved_bytes(dm);
   b.ws_bytes = moe_workspace_bytes(dm);

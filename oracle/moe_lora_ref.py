@@ -69,6 +69,7 @@ __all__ = [
     "topk_softmax",
     "route",
     "route_naive",
+    "gather_rows",
     "silu",
     "expert_forward",
     "forward",
@@ -136,6 +137,13 @@ def topk_softmax(logits: np.ndarray, k: int):
     logits are ordered by ascending expert id.  w[t, j] is the softmax of the k
     selected logits, evaluated in float64 relative to the largest one and
     rounded to float32.
+
+    Non-finite logits (outside what the pages consider): NaN ranks below every
+    other value, -inf included, and NaNs tie with each other (lower id first),
+    so every id is a valid expert.  The weights of a token whose selected
+    logits are not all finite are whatever the softmax formula gives (NaN when
+    a NaN or an infinite maximum enters).  numpy's sort places NaN keys last,
+    which is exactly this order for the negated logits.
     """
     L = np.asarray(logits, dtype=np.float32)
     T, E = L.shape
@@ -186,6 +194,20 @@ def route(topk_ids: np.ndarray, E: int) -> Routing:
     pair_pos[sorted_pair] = np.arange(flat.size)
     return Routing(counts.astype(np.int32), offsets.astype(np.int32),
                    sorted_pair.astype(np.int32), pair_pos.astype(np.int32))
+
+
+def gather_rows(R: Routing, topk_w: np.ndarray, T: int, k: int, n_shared: int = 0):
+    """The gather step of the recipe [ROUTE]: the token and routing weight of
+    every sorted row.  Row p < T*k holds pair sorted_pair[p] = t*k + j, i.e.
+    token t with weight topk_w[t, j]; with a shared expert, rows T*k + t follow,
+    token t with weight 1."""
+    sp = R.sorted_pair.astype(np.int64)
+    tok = sp // k
+    wgt = np.asarray(topk_w, dtype=np.float32).reshape(-1)[sp]
+    if n_shared:
+        tok = np.concatenate([tok, np.arange(T)])
+        wgt = np.concatenate([wgt, np.ones(T, np.float32)])
+    return tok.astype(np.int32), wgt.astype(np.float32)
 
 
 def route_naive(topk_ids: np.ndarray, E: int):
@@ -454,7 +476,7 @@ def lora_grads_expert(inp, topk_ids, topk_w, dims, e, dtype=np.float64):
 # Gradients that reach the router (beyond the pages' frozen router)
 # ----------------------------------------------------------------------------
 
-def router_grads(inp, topk_ids, topk_w, dims, dtype=np.float64):
+def router_grads(inp, topk_ids, topk_w, dims, dtype=np.float64, fw=None):
     """Routing-weight and logit gradients of the layer, given dY (``inp.dy``).
 
     Y[t] is linear in the routing weights, so
@@ -464,9 +486,12 @@ def router_grads(inp, topk_ids, topk_w, dims, dtype=np.float64):
       d_logits[t, ids[t, i]] = w[t, i] (d_topk_w[t, i] - sum_j w[t, j] d_topk_w[t, j]),
     and the logits of experts not selected get 0 (a small change leaves the
     selection as it is).  The shared expert's weight is the constant 1.
+    ``fw`` may pass the result of ``forward`` on the same arguments, whose
+    per-pair outputs O are then reused.
     """
     T, k = dims.T, dims.k
-    fw = forward(inp, topk_ids, topk_w, dims, dtype)
+    if fw is None:
+        fw = forward(inp, topk_ids, topk_w, dims, dtype)
     dY = decode(inp, "dy", dtype)
     o = fw["o_pair"][:T * k].reshape(T, k, dims.d)
     dw = (dY[:, None, :] * o).sum(axis=2)

@@ -56,3 +56,42 @@ def relerr(got, ref) -> float:
     if scale == 0:
         return float(np.max(np.abs(got)))
     return float(np.max(np.abs(got - ref)) / scale)
+
+
+def relerr_per_expert(got, ref) -> float:
+    """The largest per-expert error of an [E_tot, ...] gradient, each expert's
+    slice normalised by its own largest reference value (a lightly loaded
+    expert's error is not hidden under a hot expert's magnitude).  An expert
+    whose reference is all zero (no rows) must be exactly zero."""
+    got = np.asarray(got, np.float64)
+    ref = np.asarray(ref, np.float64)
+    worst = 0.0
+    for e in range(ref.shape[0]):
+        scale = np.max(np.abs(ref[e]))
+        if scale == 0:
+            if np.any(got[e] != 0):
+                return float("inf")
+            continue
+        worst = max(worst, float(np.max(np.abs(got[e] - ref[e])) / scale))
+    return worst
+
+
+LORA_GRADS = ("da_gu", "db_gu", "da_dn", "db_dn")
+
+
+def compare_layer(got: dict, fw: dict, bw: dict, rgr: dict) -> dict:
+    """Errors of every output against the oracle: whole-tensor norm for Y, dX
+    and the router gradients, per-expert norm for the LoRA gradients.  Every
+    element must be finite (outputs are pre-filled with NaN)."""
+    ref = {"y": fw["y"], "dx": bw["dx"], "da_gu": bw["da_gu"], "db_gu": bw["db_gu"],
+           "da_dn": bw["da_dn"], "db_dn": bw["db_dn"]}
+    if rgr is not None:
+        ref["d_topk_w"] = rgr["d_topk_w"]
+        ref["d_logits"] = rgr["d_logits"]
+    errs = {}
+    for key, r in ref.items():
+        a = to_numpy_f64(got[key])
+        assert a.shape == r.shape, (key, a.shape, r.shape)
+        assert np.all(np.isfinite(a)), f"{key}: unwritten or non-finite elements"
+        errs[key] = relerr_per_expert(a, r) if key in LORA_GRADS else relerr(a, r)
+    return errs

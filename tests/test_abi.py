@@ -63,7 +63,27 @@ BAD = [
     (dict(lora_scale=float("inf")), 1), (dict(lora_scale=float("nan")), 1),
     (dict(d=96), 2), (dict(n=100), 2), (dict(E=300, k=2), 2), (dict(r=129), 2),
     (dict(T=1 << 29, k=8), 2), (dict(dtype=2), 1), (dict(dtype=-1), 1),
+    # per-row buffers of 2 GiB or more are outside the 32-bit buffer offsets:
+    # O [P_tot, d] = 32768*8 rows x 4096 x 2 B = 2 GiB exactly
+    (dict(T=32768, d=4096, n=64, E=8, k=8), 2),
+    # G [P_tot, 2n] = 262144 x 8192 x 2 B = 4 GiB
+    (dict(T=32768, d=128, n=4096, E=8, k=8), 2),
+    # O = 8 GiB
+    (dict(T=65536, d=8192, n=64, E=8, k=8), 2),
+    # the shared expert's rows count too: (8192*8 + 8192) x 16384 x 2 B = 2.25 GiB
+    (dict(T=8192, d=16384, n=64, E=8, k=8, n_shared=1), 2),
 ]
+
+
+def test_envelope_just_inside_is_accepted(lib):
+    # [P_tot, d] one row short of 2 GiB: 262143 rows would be needed; use
+    # P_tot = 32767*8 rows of d = 4096 -> 2 GiB - 64 KiB
+    dm = _dims(T=32767, d=4096, n=64, E=8, k=8)
+    assert lib.moe_workspace_bytes(ctypes.byref(dm)) > 0
+    dm = _dims(T=32768, d=2048, n=2048, E=8, k=8)  # G = 262144 x 4096 x 2 B = 2 GiB
+    assert lib.moe_workspace_bytes(ctypes.byref(dm)) == 0
+    dm = _dims(T=32768, d=2048, n=2047 // 64 * 64, E=8, k=8)
+    assert lib.moe_workspace_bytes(ctypes.byref(dm)) > 0
 
 
 @pytest.mark.parametrize("kw,code", BAD)
@@ -72,7 +92,7 @@ def test_invalid_dims_rejected_on_host(lib, kw, code):
     assert lib.moe_workspace_bytes(ctypes.byref(dm)) == 0
     assert lib.moe_forward_saved_bytes(ctypes.byref(dm)) == 0
     fake = ctypes.c_void_p(4096)  # never dereferenced: validation fails first
-    rt = _lib.MoeRouting(*([4096] * 6))
+    rt = _lib.MoeRouting(*([4096] * 8))
     assert lib.moe_route(ctypes.byref(dm), fake, ctypes.byref(rt), fake, 1 << 40, None) == code
     w = _lib.MoeWeights(*([4096] * 6))
     assert lib.moe_lora_forward(ctypes.byref(dm), fake, ctypes.byref(rt), ctypes.byref(w), fake,
@@ -82,7 +102,7 @@ def test_invalid_dims_rejected_on_host(lib, kw, code):
 def test_null_misaligned_and_small_buffers_rejected(lib):
     dm = _dims()
     fake = 4096
-    rt = _lib.MoeRouting(*([fake] * 6))
+    rt = _lib.MoeRouting(*([fake] * 8))
     w = _lib.MoeWeights(*([fake] * 6))
     big = 1 << 40
     # null dims
@@ -90,8 +110,14 @@ def test_null_misaligned_and_small_buffers_rejected(lib):
     # null / misaligned pointers
     assert lib.moe_route(ctypes.byref(dm), None, ctypes.byref(rt), fake, big, None) == 1
     assert lib.moe_route(ctypes.byref(dm), fake + 4, ctypes.byref(rt), fake, big, None) == 1
-    bad_rt = _lib.MoeRouting(fake, fake, fake, 0, fake, fake)
-    assert lib.moe_route(ctypes.byref(dm), fake, ctypes.byref(bad_rt), fake, big, None) == 1
+    for i in range(8):  # every routing pointer is required and 16-byte aligned
+        ptrs = [fake] * 8
+        ptrs[i] = 0
+        assert lib.moe_route(ctypes.byref(dm), fake, ctypes.byref(_lib.MoeRouting(*ptrs)), fake, big,
+                             None) == 1
+        ptrs[i] = fake + 8
+        assert lib.moe_route(ctypes.byref(dm), fake, ctypes.byref(_lib.MoeRouting(*ptrs)), fake, big,
+                             None) == 1
     bad_w = _lib.MoeWeights(fake, fake, fake + 2, fake, fake, fake)
     assert lib.moe_lora_forward(ctypes.byref(dm), fake, ctypes.byref(rt), ctypes.byref(bad_w), fake,
                                 fake, big, fake, big, None) == 1

@@ -1,11 +1,16 @@
 """Full-size workloads on the GPU, in the launch configuration bench.py times,
-checked against the oracle on outputs it can compute one by one: Y, dX and
-router-gradient rows of sampled tokens (float64), and the LoRA gradients of
-sampled experts (float32: the least-loaded expert with rows, an empty expert
-when there is one, the most-loaded expert, and the shared expert when there
-is one), and a rerun in the same buffers must reproduce every output bit for
-bit.  The headline shape runs again with fp16 elements.
-Routing at these sizes is compared in full by test_gpu_route."""
+compared element by element with the float32 oracle: every element of Y, dX,
+the four LoRA gradients (each expert's slice normed by itself) and the
+routing-weight and logit gradients, with every reference computed from the
+oracle's own routing (top-k ids equal to the GPU's bit for bit, routing
+weights the oracle's).  A rerun in the same buffers must reproduce every
+output bit for bit.  The headline shape runs again with fp16 elements.
+Routing at these sizes is compared in full by test_gpu_route.
+
+Oracle time on 16 host threads (float32 numpy, forward + backward): about 2 s
+for qwen3_30b_a3b, 3 s for deepseek_shared and 10-20 s each for long_zipf and
+routing_stress."""
+import time
 from dataclasses import replace
 
 import numpy as np
@@ -14,7 +19,7 @@ import torch
 
 import mixture_experts_lora_amd as mel
 import oracle
-from gpu_helpers import TOL, announce, mdims, relerr, require_gpu, to_numpy_f64, upload
+from gpu_helpers import TOL, announce, compare_layer, mdims, require_gpu, upload
 from synth import CONFIGS, make_inputs
 
 pytestmark = pytest.mark.gpu
@@ -25,7 +30,7 @@ FULL["qwen3_30b_a3b_f16"] = replace(CONFIGS["qwen3_30b_a3b"], element="f16")
 
 
 @pytest.mark.parametrize("name", list(FULL))
-def test_full_size_sampled(name):
+def test_full_size_every_element(name):
     require_gpu()
     ld = FULL[name]
     announce("full", name, ld)
@@ -33,40 +38,17 @@ def test_full_size_sampled(name):
     dims = mdims(ld)
     logits, x, dy, w = upload(inp)
     layer = mel.MoELoRALayer(dims, w)
+    layer.y.fill_(float("nan"))
     for t in layer.grads:
         t.fill_(float("nan"))
     layer.route(logits)
     y = layer.forward(x)
     g = layer.backward(dy, x, router=True)
     torch.cuda.synchronize()
-    ids = layer.routing.topk_ids.cpu().numpy()
-    tw = layer.routing.topk_w.cpu().numpy()
-    np.testing.assert_array_equal(ids, oracle.topk_softmax(inp.logits, ld.k)[0])
-    rng = np.random.default_rng(7)
-    toks = sorted(set([0, ld.T - 1] + rng.choice(ld.T, 4, replace=False).tolist()))
-    y_ref = oracle.forward_tokens(inp, ids, tw, ld, toks)
-    dx_ref = oracle.backward_tokens(inp, ids, tw, ld, toks)
-    ey = relerr(to_numpy_f64(y)[toks], y_ref)
-    edx = relerr(to_numpy_f64(g.dx)[toks], dx_ref)
-    r_ref = oracle.router_grads_tokens(inp, ids, tw, ld, toks)
-    edw = relerr(to_numpy_f64(layer.router_grads.d_topk_w)[toks], r_ref["d_topk_w"])
-    edl = relerr(to_numpy_f64(layer.router_grads.d_logits)[toks], r_ref["d_logits"])
-    print(f"Y rows {ey:.2e}  dX rows {edx:.2e}  d_topk_w rows {edw:.2e}  d_logits rows {edl:.2e}",
-          flush=True)
-    assert ey <= TOL and edx <= TOL and edw <= TOL and edl <= TOL
-    counts = np.bincount(ids.reshape(-1), minlength=ld.E)
-    experts = {int(np.argmin(np.where(counts > 0, counts, 1 << 30))), int(np.argmax(counts))}
-    if np.any(counts == 0):
-        experts.add(int(np.argmin(counts)))
-    if ld.n_shared:
-        experts.add(ld.E)
-    got = [to_numpy_f64(t) for t in (g.da_gate_up, g.db_gate_up, g.da_down, g.db_down)]
-    for a in got:
-        assert np.all(np.isfinite(a)), "unwritten or non-finite gradient elements"
-    # a second route + forward + backward in the same buffers gives bitwise the
-    # same outputs (no atomics, no order that depends on timing)
     first = [t.clone() for t in (y, g.dx, g.da_gate_up, g.db_gate_up, g.da_down, g.db_down,
                                  layer.router_grads.d_topk_w, layer.router_grads.d_logits)]
+    # a second route + forward + backward in the same buffers gives bitwise the
+    # same outputs (no atomics, no order that depends on timing)
     layer.route(logits)
     layer.forward(x)
     layer.backward(dy, x, router=True)
@@ -75,10 +57,19 @@ def test_full_size_sampled(name):
              layer.router_grads.d_topk_w, layer.router_grads.d_logits)
     for a, b in zip(first, again):
         assert torch.equal(a, b), "a rerun changed an output"
-    for e in sorted(experts):
-        ref = oracle.lora_grads_expert(inp, ids, tw, ld, e, dtype=np.float32)
-        errs = [relerr(a[e], b) if np.any(b) else float(np.max(np.abs(a[e]))) for a, b in zip(got, ref)]
-        print(f"expert {e} rows {counts[e] if e < ld.E else ld.T}: " + " ".join(f"{v:.2e}" for v in errs),
-              flush=True)
-        for v in errs:
-            assert v <= TOL, (e, errs)
+
+    t0 = time.perf_counter()
+    ids, tw = oracle.topk_softmax(inp.logits, ld.k)
+    np.testing.assert_array_equal(layer.routing.topk_ids.cpu().numpy(), ids)
+    np.testing.assert_allclose(layer.routing.topk_w.cpu().numpy(), tw, rtol=2e-6, atol=1e-7)
+    fw = oracle.forward(inp, ids, tw, ld, dtype=np.float32)
+    bw = oracle.backward(inp, ids, tw, ld, dtype=np.float32)
+    rgr = oracle.router_grads(inp, ids, tw, ld, dtype=np.float32, fw=fw)
+    print(f"oracle {time.perf_counter() - t0:.1f} s", flush=True)
+    got = {"y": y, "dx": g.dx, "da_gu": g.da_gate_up, "db_gu": g.db_gate_up,
+           "da_dn": g.da_down, "db_dn": g.db_down, "d_topk_w": layer.router_grads.d_topk_w,
+           "d_logits": layer.router_grads.d_logits}
+    errs = compare_layer(got, fw, bw, rgr)
+    print("errors", {k: f"{v:.2e}" for k, v in errs.items()}, flush=True)
+    for key, e in errs.items():
+        assert e <= TOL, (key, e)

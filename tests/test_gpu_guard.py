@@ -56,7 +56,8 @@ def _run_guarded(dims, logits, x, dy, w):
     d, n, r = dims.d, dims.n, dims.r
     i32, f32 = torch.int32, torch.float32
     rt = mel.Routing(A.take((T, k), i32), A.take((T, k), f32), A.take((E,), i32),
-                     A.take((E + 1,), i32), A.take((P,), i32), A.take((P,), i32))
+                     A.take((E + 1,), i32), A.take((P,), i32), A.take((P,), i32),
+                     A.take((dims.P_tot,), i32), A.take((dims.P_tot,), f32))
     rws = A.take((mel.route_workspace_bytes(dims),), torch.uint8)
     saved = A.take((mel.forward_saved_bytes(dims),), torch.uint8)
     ws = A.take((mel.workspace_bytes(dims),), torch.uint8)

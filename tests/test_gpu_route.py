@@ -1,5 +1,7 @@
 """Routing on the GPU against the oracle: top-k ids, counts, offsets,
-sorted_pair and pair_pos bit-exact; routing weights to fp32 rounding."""
+sorted_pair, pair_pos and the gather table's tokens bit-exact; routing weights
+(and the gather table's weights) to fp32 rounding; NaN and infinite logits
+give the oracle's ids."""
 import numpy as np
 import pytest
 import torch
@@ -24,14 +26,25 @@ def _run_and_compare(dims_l, logits_np):
     torch.cuda.synchronize()
     ids, w = oracle.topk_softmax(logits_np, dims.k)
     R = oracle.route(ids, dims.E)
+    tok, wgt = oracle.gather_rows(R, w, dims.T, dims.k, dims.n_shared)
     np.testing.assert_array_equal(rt.topk_ids.cpu().numpy(), ids)
     np.testing.assert_array_equal(rt.counts.cpu().numpy(), R.counts)
     np.testing.assert_array_equal(rt.offsets.cpu().numpy(), R.offsets)
     np.testing.assert_array_equal(rt.sorted_pair.cpu().numpy(), R.sorted_pair)
     np.testing.assert_array_equal(rt.pair_pos.cpu().numpy(), R.pair_pos)
-    np.testing.assert_allclose(rt.topk_w.cpu().numpy(), w, rtol=2e-6, atol=1e-7)
+    np.testing.assert_array_equal(rt.row_token.cpu().numpy(), tok)
+    gw, gr = rt.topk_w.cpu().numpy(), rt.row_weight.cpu().numpy()
+    fin = np.isfinite(w)
+    np.testing.assert_array_equal(np.isfinite(gw), fin)
+    np.testing.assert_allclose(gw[fin], w[fin], rtol=2e-6, atol=1e-7)
+    np.testing.assert_array_equal(np.isfinite(gr), np.isfinite(wgt))
+    # the gather table carries the same fp32 weights the GPU wrote into topk_w
+    sp = R.sorted_pair.astype(np.int64)
+    np.testing.assert_array_equal(gr[:dims.P], gw.reshape(-1)[sp])
+    if dims.n_shared:
+        assert np.all(gr[dims.P:] == 1.0)
     for a, b in zip(rt, again):  # deterministic
-        assert torch.equal(a, b)
+        assert torch.equal(a.view(torch.int32), b.view(torch.int32))
 
 
 @pytest.mark.parametrize("name", list(CONFIGS))
@@ -49,6 +62,10 @@ EDGE = [
     LayerDims(777, 64, 64, 256, 8, 4),    # widest E
     LayerDims(64, 64, 64, 256, 256, 4),   # k = E = 256
     LayerDims(1000, 64, 64, 37, 5, 4),    # E not a power of two
+    LayerDims(4097, 64, 64, 16, 4, 4),    # two rounds of 16 tokens per block, ragged last block
+    LayerDims(70000, 64, 64, 256, 8, 4),  # many rounds per block, several blocks per scatter group
+    LayerDims(333, 64, 64, 6, 2, 4, n_shared=1),  # gather table with the shared expert's rows
+    LayerDims(5000, 64, 64, 64, 4, 4, n_shared=1),
 ]
 
 
@@ -68,3 +85,20 @@ def test_route_ties_and_one_hot_expert():
     L2 = np.zeros((200, 6), np.float32)
     L2[:, 4] = 3.0
     _run_and_compare(LayerDims(200, 64, 64, 6, 2, 4), L2)
+
+
+def test_route_nan_and_infinite_logits():
+    """Non-finite logits still give valid ids, the oracle's order (NaN below
+    -inf), and a consistent grouping."""
+    announce("route nan")
+    rng = np.random.default_rng(12)
+    L = rng.normal(size=(300, 24)).astype(np.float32)
+    L[0] = np.nan
+    L[1, :20] = np.nan
+    L[2, [3, 7]] = -np.inf
+    L[2, [1, 5]] = np.nan
+    L[3, 4] = np.inf
+    L[4, ::2] = np.nan
+    L[5] = -np.inf
+    L[17::23, 5] = np.nan
+    _run_and_compare(LayerDims(300, 64, 64, 24, 6, 4), L)

@@ -125,3 +125,55 @@ def test_zipf_recipe_marginals():
     # Gumbel-top-k: the first pick is expert e with probability p_e
     first = np.bincount(ids[:, 0], minlength=32) / dims.T
     assert abs(first.max() - p_top) < 0.015
+
+
+def _brute_topk_nan(L, k):
+    """Full per-row sort with NaN below every number (-inf included)."""
+    T, E = L.shape
+
+    def key(t, e):
+        v = float(L[t, e])
+        return (0, 0.0, e) if v != v else (-1, -v, e)
+    return np.array([sorted(range(E), key=lambda e: key(t, e))[:k] for t in range(T)],
+                    dtype=np.int32)
+
+
+def test_topk_nan_and_infinite_logits():
+    rng = np.random.default_rng(11)
+    L = rng.normal(size=(40, 12)).astype(np.float32)
+    L[0] = np.nan                                  # a diverged router row
+    L[1, :10] = np.nan                             # fewer finite logits than k
+    L[2, [3, 7]] = -np.inf
+    L[2, [1, 5]] = np.nan                          # NaN below -inf
+    L[3, 4] = np.inf
+    L[4, ::2] = np.nan
+    L[5] = -np.inf
+    for k in (1, 3, 4, 12):
+        ids, w = oracle.topk_softmax(L, k)
+        np.testing.assert_array_equal(ids, _brute_topk_nan(L, k))
+        assert ids.min() >= 0 and ids.max() < 12
+        R = oracle.route(ids, 12)
+        assert int(R.counts.sum()) == 40 * k
+        fin = np.all(np.isfinite(np.take_along_axis(L, ids.astype(np.int64), 1)), axis=1)
+        assert np.all(np.isfinite(w[fin]))
+        np.testing.assert_allclose(w[fin].sum(axis=1), 1.0, atol=1e-6)
+    ids, _ = oracle.topk_softmax(L, 3)
+    assert ids[0].tolist() == [0, 1, 2]            # all NaN: lowest ids
+    assert ids[1].tolist() == [10, 11, 0]          # the two numbers, then the lowest NaN
+    assert ids[2, 2] not in (1, 5)
+
+
+@pytest.mark.parametrize("S", [0, 1])
+def test_gather_rows_follow_the_per_expert_search(S):
+    dims = LayerDims(37, 64, 64, 7, 3, 4, n_shared=S)
+    ids, w = oracle.topk_softmax(make_logits(dims, seed=4), dims.k)
+    R = oracle.route(ids, dims.E)
+    tok, wgt = oracle.gather_rows(R, w, dims.T, dims.k, S)
+    assert tok.shape == (dims.P_tot,) and wgt.shape == (dims.P_tot,)
+    for e, (t_e, s_e) in enumerate(oracle.route_naive(ids, dims.E)):
+        seg = slice(R.offsets[e], R.offsets[e + 1])
+        np.testing.assert_array_equal(tok[seg], t_e)
+        np.testing.assert_array_equal(wgt[seg], w[t_e, s_e])
+    if S:
+        np.testing.assert_array_equal(tok[dims.P:], np.arange(dims.T))
+        assert np.all(wgt[dims.P:] == 1.0)
