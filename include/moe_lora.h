@@ -157,6 +157,23 @@ size_t moe_workspace_bytes(const moe_dims* dims);
 moe_status moe_route(const moe_dims* dims, const float* logits, const moe_routing* out,
                      void* ws, size_t ws_bytes, void* stream);
 
+/* moe_route for callers that cannot allocate device memory: code under HIP
+ * graph capture, tight serving loops, harnesses that forbid allocation.  It
+ * takes no workspace: its scratch is a MOE_ROUTE_NOALLOC_SCRATCH_BYTES (4 MiB)
+ * array of device memory that the library holds on each GPU it runs on until
+ * the process ends, looked up once per device on the first call.  The call
+ * allocates nothing, on the device or on the host.
+ *   Limit: moe_route_workspace_bytes(dims) <= 4 MiB (about T*k <= 983,040 at
+ *   E = 256); a larger shape returns MOE_ERROR_UNSUPPORTED with nothing
+ *   enqueued.  MOE_ERROR_LAUNCH if the device copy of the array cannot be
+ *   found.  Otherwise arguments, outputs and errors are those of moe_route.
+ *   Every call on one GPU uses that GPU's one array: calls that overlap on a
+ *   GPU (on different streams, or from different threads) race and must be
+ *   ordered by the caller. */
+#define MOE_ROUTE_NOALLOC_SCRATCH_BYTES (4u << 20)
+moe_status moe_route_noalloc(const moe_dims* dims, const float* logits, const moe_routing* out,
+                             void* stream);
+
 /* Forward of the expert layer with split LoRA (faster-MoE page, "What is
  * torch._grouped_mm?" and "Faster LoRA MoE training"):
  *   for each routed pair (t, j) with expert e = topk_ids[t,j]:

@@ -27,6 +27,7 @@ from .api import (  # noqa: F401
     forward_saved_bytes,
     get_engines,
     route,
+    route_noalloc,
     route_workspace_bytes,
     set_engines,
     workspace_bytes,

@@ -16,12 +16,15 @@ MOE_ERROR_LAUNCH = 4
 MOE_BF16 = 0
 MOE_F16 = 1
 
+MOE_ROUTE_NOALLOC_SCRATCH_BYTES = 4 << 20
+
 EXPORTED = (
     "moe_status_string",
     "moe_route_workspace_bytes",
     "moe_forward_saved_bytes",
     "moe_workspace_bytes",
     "moe_route",
+    "moe_route_noalloc",
     "moe_lora_forward",
     "moe_lora_backward",
     "moe_set_engines",
@@ -80,6 +83,8 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
         getattr(lib, q).argtypes = [pd]
     lib.moe_route.restype = ctypes.c_int
     lib.moe_route.argtypes = [pd, vp, pr, vp, sz, vp]
+    lib.moe_route_noalloc.restype = ctypes.c_int
+    lib.moe_route_noalloc.argtypes = [pd, vp, pr, vp]
     lib.moe_lora_forward.restype = ctypes.c_int
     lib.moe_lora_forward.argtypes = [pd, vp, pr, pw, vp, vp, sz, vp, sz, vp]
     lib.moe_lora_backward.restype = ctypes.c_int

@@ -200,6 +200,20 @@ def route(logits: torch.Tensor, dims: Dims, out: Optional[Routing] = None,
     return out
 
 
+def route_noalloc(logits: torch.Tensor, dims: Dims, out: Routing, stream=None) -> Routing:
+    """moe_route_noalloc: routing into caller-owned buffers with the library's
+    own per-GPU scratch (no workspace; nothing is allocated).  Calls that
+    overlap on one GPU race."""
+    lib = _lib.load()
+    _check(logits, (dims.T, dims.E), torch.float32, "logits")
+    _check_routing(out, dims)
+    dc, rc = dims.c(), _c_routing(out)
+    with _on(stream) as s:
+        _lib.check(lib.moe_route_noalloc(ctypes.byref(dc), logits.data_ptr(), ctypes.byref(rc), s),
+                   "moe_route_noalloc")
+    return out
+
+
 def forward(x: torch.Tensor, routing: Routing, weights: Weights, dims: Dims,
             y: Optional[torch.Tensor] = None, saved: Optional[torch.Tensor] = None,
             ws: Optional[torch.Tensor] = None, stream=None):
