@@ -34,6 +34,7 @@ constexpr int RS_THREADS = RS_TOK * 16;
 constexpr int RS_MAXBLK = 256;          // route_select workgroups at most
 constexpr int SC_THREADS = 1024;        // route_scatter workgroup
 constexpr int SC_MAXBLK = 64;           // route_scatter workgroups at most
+constexpr int SC_BPB = RS_MAXBLK / SC_MAXBLK;  // histogram rows per route_scatter workgroup at most
 
 struct RouteGeom {
   int spb;    // rounds of 16 tokens per route_select workgroup
@@ -94,6 +95,10 @@ __device__ __forceinline__ float row_sum(float x) {
   return x;
 }
 
+__device__ __forceinline__ uint64_t max64(uint64_t a, uint64_t b) { return a > b ? a : b; }
+
+// NV keys per lane (the smallest power of two with 16 NV >= E)
+template <int NV>
 __global__ __launch_bounds__(RS_THREADS) void route_select(
     const float* __restrict__ logits, int T, int E, int k, int spb, int32_t* __restrict__ topk_ids,
     float* __restrict__ topk_w, int32_t* __restrict__ blk_counts, int32_t* __restrict__ local_rank) {
@@ -107,7 +112,6 @@ __global__ __launch_bounds__(RS_THREADS) void route_select(
     cnt[e] = 0;
   }
   __syncthreads();
-  const int nv = (E + 15) >> 4;  // keys per lane
 #pragma unroll 1
   for (int s = 0; s < spb; ++s) {
     const int64_t t0 = ((int64_t)blockIdx.x * spb + s) * RS_TOK;
@@ -115,22 +119,31 @@ __global__ __launch_bounds__(RS_THREADS) void route_select(
     const int64_t t = t0 + tl;
     const bool valid = t < T;
     // lane sub keeps the keys of experts sub, sub + 16, ...; absent ones are 0
-    uint64_t key[16];
+    float lv[NV];
 #pragma unroll
-    for (int i = 0; i < 16; ++i) {
+    for (int i = 0; i < NV; ++i) {
       const int e = sub + 16 * i;
-      key[i] = 0;
-      if (i < nv && valid && e < E)
-        key[i] = ((uint64_t)rt_ord(logits[t * E + e]) << 32) | (uint64_t)(0xffffffffu - (uint32_t)e);
+      lv[i] = valid && e < E ? logits[t * E + e] : 0.0f;
+    }
+    uint64_t key[NV];
+#pragma unroll
+    for (int i = 0; i < NV; ++i) {
+      const int e = sub + 16 * i;
+      key[i] = valid && e < E ? ((uint64_t)rt_ord(lv[i]) << 32) | (uint64_t)(0xffffffffu - (uint32_t)e) : 0;
     }
     uint64_t prev = ~(uint64_t)0;
 #pragma unroll 1
     for (int j = 0; j < k; ++j) {
-      uint64_t best = 0;
+      // the lane's largest key below the previous pick: independent
+      // candidates, then a tree of maxima
+      uint64_t c[NV];
 #pragma unroll
-      for (int i = 0; i < 16; ++i)
-        if (i < nv) best = (key[i] < prev && key[i] > best) ? key[i] : best;
-      best = row_max64(best);
+      for (int i = 0; i < NV; ++i) c[i] = key[i] < prev ? key[i] : 0;
+#pragma unroll
+      for (int w = NV / 2; w >= 1; w >>= 1)
+#pragma unroll
+        for (int i = 0; i < w; ++i) c[i] = max64(c[i], c[i + w]);
+      const uint64_t best = row_max64(c[0]);
       prev = best;
       if (sub == (j & 15)) sel[tl * k + j] = best;
     }
@@ -166,6 +179,9 @@ __global__ __launch_bounds__(RS_THREADS) void route_select(
   for (int e = threadIdx.x; e < E; e += RS_THREADS) blk_counts[(int64_t)blockIdx.x * E + e] = cnt[e];
 }
 
+constexpr int SC_PRE = 4;                 // pairs per thread whose inputs load with the histogram
+constexpr int SC_COL = 32;                // histogram rows per load batch of the column sums
+
 __global__ __launch_bounds__(SC_THREADS) void route_scatter(
     const int32_t* __restrict__ topk_ids, const float* __restrict__ topk_w,
     const int32_t* __restrict__ blk_counts, const int32_t* __restrict__ local_rank, int T, int E, int k,
@@ -174,71 +190,92 @@ __global__ __launch_bounds__(SC_THREADS) void route_scatter(
     float* __restrict__ row_weight) {
   __shared__ int part_lo[SC_THREADS];   // [group][expert] histogram rows below this range
   __shared__ int part_tot[SC_THREADS];  // [group][expert] all histogram rows
-  __shared__ int base[256];             // pairs of expert e before the current block
-  __shared__ int off[256 + 1];
+  __shared__ int base[SC_BPB][256];     // offsets[e] + pairs of e in rows before row q of the range
   __shared__ int sh[SC_THREADS / 64];
   const int tid = threadIdx.x;
   const int bfirst = blockIdx.x * bpb2, blast = min(nblk, bfirst + bpb2);
-  // column sums of the histogram, rows split over ng groups of E threads
+  const int64_t tok_per_blk = (int64_t)spb * RS_TOK;
+  const int64_t ta = bfirst * tok_per_blk, tb = min((int64_t)T, blast * tok_per_blk);
+  const int64_t i_end = tb * k;
+  // Every global load the placement needs is issued here, before any result
+  // is used: the thread's first SC_PRE pairs, its histogram column chunk and
+  // (threads e < E) expert e's entries in the range's rows.
+  int p_id[SC_PRE], p_rank[SC_PRE];
+  float p_w[SC_PRE];
+#pragma unroll
+  for (int q = 0; q < SC_PRE; ++q) {
+    const int64_t i = ta * k + tid + (int64_t)q * SC_THREADS;
+    const bool ok = i < i_end;
+    p_id[q] = ok ? topk_ids[i] : 0;
+    p_rank[q] = ok ? local_rank[i] : 0;
+    p_w[q] = ok ? topk_w[i] : 0.0f;
+  }
+  // column sums of the histogram: rows split over ng groups of E threads
   const int ng = SC_THREADS / E;
   const int g = tid / E, e = tid - g * E;
+  // (nblk <= 256 rows and ng >= 8 groups for E <= 128: one batch; two at E = 256)
+  const int ch = cdiv(nblk, ng);
+  const int r0 = g * ch, r1 = g < ng ? min(nblk, r0 + ch) : r0;
+  int rowc[SC_BPB];
+#pragma unroll
+  for (int q = 0; q < SC_BPB; ++q)
+    rowc[q] = tid < E && bfirst + q < blast ? blk_counts[(int64_t)(bfirst + q) * E + tid] : 0;
   int lo = 0, tot = 0;
-  if (g < ng) {
-    const int ch = cdiv(nblk, ng);
-    const int r0 = g * ch, r1 = min(nblk, r0 + ch);
-#pragma unroll 8
-    for (int rb = r0; rb < r1; ++rb) {
-      const int c = blk_counts[(int64_t)rb * E + e];
-      tot += c;
-      lo += rb < bfirst ? c : 0;
+  for (int rb = r0; rb < r1; rb += SC_COL) {
+    int c[SC_COL];
+#pragma unroll
+    for (int q = 0; q < SC_COL; ++q) c[q] = rb + q < r1 ? blk_counts[(int64_t)(rb + q) * E + e] : 0;
+#pragma unroll
+    for (int q = 0; q < SC_COL; ++q) {
+      tot += c[q];
+      lo += rb + q < bfirst ? c[q] : 0;
     }
   }
   part_lo[tid] = lo;
   part_tot[tid] = tot;
   __syncthreads();
-  int c_e = 0;
+  int c_e = 0, below = 0;
   if (tid < E) {
-    int l = 0;
     for (int gg = 0; gg < ng; ++gg) {
-      l += part_lo[gg * E + tid];
+      below += part_lo[gg * E + tid];
       c_e += part_tot[gg * E + tid];
     }
-    base[tid] = l;
   }
   int total;
   const int o = block_excl_scan<SC_THREADS / 64>(c_e, sh, &total);
   if (tid < E) {
-    off[tid] = o;
+    // first sorted position of expert e's pairs in each histogram row of the range
+    int run = o + below;
+#pragma unroll
+    for (int q = 0; q < SC_BPB; ++q) {
+      base[q][tid] = run;
+      run += rowc[q];
+    }
     if (blockIdx.x == 0) {
       counts[tid] = c_e;
       offsets[tid] = o;
     }
   }
-  if (tid == 0) {
-    off[E] = total;
-    if (blockIdx.x == 0) offsets[E] = total;
-  }
+  if (tid == 0 && blockIdx.x == 0) offsets[E] = total;
   __syncthreads();
-  const int64_t tok_per_blk = (int64_t)spb * RS_TOK;
-#pragma unroll 1
-  for (int rb = bfirst; rb < blast; ++rb) {
-    const int64_t i0 = rb * tok_per_blk * k;
-    const int64_t i1 = min((int64_t)T, (rb + 1) * tok_per_blk) * k;
-    for (int64_t i = i0 + tid; i < i1; i += SC_THREADS) {
-      const int id = topk_ids[i];
-      const int dest = off[id] + base[id] + local_rank[i];
-      sorted_pair[dest] = (int32_t)i;
-      pair_pos[i] = dest;
-      row_token[dest] = (int32_t)(i / k);
-      row_weight[dest] = topk_w[i];
-    }
-    __syncthreads();  // every thread has read base before it moves on
-    if (tid < E) base[tid] += blk_counts[(int64_t)rb * E + tid];
-    __syncthreads();
+  auto place = [&](int64_t i, int id, int rank, float w) {
+    const int64_t t = i / k;
+    const int q = (int)(t / tok_per_blk) - bfirst;
+    const int dest = base[q][id] + rank;
+    sorted_pair[dest] = (int32_t)i;
+    pair_pos[i] = dest;
+    row_token[dest] = (int32_t)t;
+    row_weight[dest] = w;
+  };
+#pragma unroll
+  for (int q = 0; q < SC_PRE; ++q) {
+    const int64_t i = ta * k + tid + (int64_t)q * SC_THREADS;
+    if (i < i_end) place(i, p_id[q], p_rank[q], p_w[q]);
   }
+  for (int64_t i = ta * k + tid + (int64_t)SC_PRE * SC_THREADS; i < i_end; i += SC_THREADS)
+    place(i, topk_ids[i], local_rank[i], topk_w[i]);
   if (S) {
     const int64_t P = (int64_t)T * k;
-    const int64_t ta = bfirst * tok_per_blk, tb = min((int64_t)T, blast * tok_per_blk);
     for (int64_t t = ta + tid; t < tb; t += SC_THREADS) {
       row_token[P + t] = (int32_t)t;
       row_weight[P + t] = 1.0f;
@@ -262,8 +299,11 @@ hipError_t launch_route(const float* logits, int64_t T, int E, int k, int S, int
   int32_t* blk = (int32_t*)ws;
   int32_t* rank = (int32_t*)((char*)ws + a);
   const size_t lds = (size_t)RS_TOK * k * sizeof(uint64_t);
-  MOE_LAUNCH("route_select", route_select, dim3(g.nblk), dim3(RS_THREADS), lds, st, logits, (int)T, E, k,
-             g.spb, ids, w, blk, rank);
+  const int nv = (E + 15) / 16;
+  auto sel = nv <= 1 ? route_select<1> : nv <= 2 ? route_select<2> : nv <= 4 ? route_select<4>
+             : nv <= 8 ? route_select<8> : route_select<16>;
+  MOE_LAUNCH("route_select", sel, dim3(g.nblk), dim3(RS_THREADS), lds, st, logits, (int)T, E, k, g.spb, ids,
+             w, blk, rank);
   MOE_LAUNCH("route_scatter", route_scatter, dim3(g.nblk2), dim3(SC_THREADS), 0, st, ids, w, blk, rank,
              (int)T, E, k, S, g.spb, g.nblk, g.bpb2, counts, offsets, sorted_pair, pair_pos, row_token,
              row_weight);
