@@ -148,6 +148,88 @@ def cpu_baseline(dims, inp, budget_s: float):
                       f"route+forward+backward, median of 3 passes = {med:.2f} s"}
 
 
+CROSSOVER_T = (1024, 2048, 4096, 8192, 12288, 16384, 24576, 32768, 49152)
+
+
+def crossover(args):
+    """Split LoRA against the merged-weight path the pages compare it with
+    (faster-MoE page, "MoE LoRA changes things"), forward only, at the
+    Qwen3-30B-A3B shapes (d 2048, n 768, E 128, top-8, r 64) for a range of
+    token counts T: the split forward (rank-r pre-passes, grouped products
+    with their low-rank pass, combine) against merging W + s (A B)^T for
+    every expert and running the grouped products on the merged weights.
+    The inputs are the first T tokens of one seeded draw; the weights are
+    the same for every T.  Prints one JSON line with the times and the
+    crossover T (linear interpolation where merged first beats split) next
+    to the page's FLOP-count formulas."""
+    import numpy as np
+    import torch
+
+    import mixture_experts_lora_amd as mel
+    from synth import CONFIGS, make_inputs
+
+    base = CONFIGS["qwen3_30b_a3b"]
+    big = dataclasses.replace(base, T=max(CROSSOVER_T))
+    inp = make_inputs(big, seed=0)
+
+    def bf(a):
+        return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).cuda().view(torch.bfloat16)
+
+    w = mel.Weights(bf(inp.w_gu), bf(inp.w_dn), bf(inp.a_gu), bf(inp.b_gu), bf(inp.a_dn), bf(inp.b_dn))
+    X, L = bf(inp.x), torch.from_numpy(inp.logits).cuda()
+    merged = mel.MergedWeights(torch.empty_like(w.w_gate_up), torch.empty_like(w.w_down))
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+
+    def timed(fn, reps):
+        for _ in range(2):
+            fn()
+        torch.cuda.synchronize()
+        e0.record()
+        for _ in range(reps):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / reps
+
+    rows = []
+    for T in CROSSOVER_T:
+        c = dataclasses.replace(base, T=T)
+        dims = mel.Dims(c.T, c.d, c.n, c.E, c.k, c.r, c.n_shared, c.lora_scale)
+        layer = mel.MoELoRALayer(dims, w)
+        x = X[:T].contiguous()
+        layer.route(L[:T].contiguous())
+        y_m = torch.empty_like(x)
+        reps = 10 if T <= 16384 else 5
+        split = timed(lambda: layer.forward(x), reps)
+        merge = timed(lambda: mel.merge_lora(w, dims, out=merged), reps)
+        fwd_m = timed(lambda: mel.forward_merged(x, layer.routing, merged, dims, y=y_m, saved=layer.saved,
+                                                 ws=layer.ws), reps)
+        both = timed(lambda: (mel.merge_lora(w, dims, out=merged),
+                              mel.forward_merged(x, layer.routing, merged, dims, y=y_m, saved=layer.saved,
+                                                 ws=layer.ws)), reps)
+        rows.append({"T": T, "split_ms": round(split, 4), "merged_ms": round(both, 4),
+                     "merge_only_ms": round(merge, 4), "merged_products_ms": round(fwd_m, 4)})
+        print(json.dumps(rows[-1]), file=sys.stderr, flush=True)
+        del layer
+        torch.cuda.empty_cache()
+    cross = None
+    for a, b in zip(rows, rows[1:]):
+        da, db = a["merged_ms"] - a["split_ms"], b["merged_ms"] - b["split_ms"]
+        if da > 0 >= db:
+            cross = round(a["T"] + (b["T"] - a["T"]) * da / (da - db))
+            break
+    E, m, n, k, r = base.E, base.d, base.n, base.k, base.r
+    out = {"metric": "split vs merged LoRA forward, ms", "config": {
+        "workload": "qwen3_30b_a3b shapes, forward only", "d": m, "n": n, "E": E, "top_k": k,
+        "lora_rank": r, "dtype": "bf16"},
+        "rows": rows, "measured_crossover_T": cross,
+        "page_formula_T": {"per projection (m, n) = (2048, 768)": round(E * m * n / (k * (m + n)) * (1 + 1 / (2 * r))),
+                           "fused gate_up (m, 2n)": round(E * m * 2 * n / (k * (m + 2 * n)) * (1 + 1 / (2 * r))),
+                           "whole layer (gate_up + down)": round(E * (2 * r + 1) * (m * 2 * n + n * m)
+                                                                 / (2 * k * r * ((m + 2 * n) + (n + m))))}}
+    print(json.dumps(out), flush=True)
+
+
 def measured_traffic(kernel: str, workload: str):
     """HBM bytes per launch of `kernel` from the committed rocprofv3 counter
     summary, or None when the kernel source changed since it was measured."""
@@ -183,6 +265,8 @@ def main():
                     help="keep the build's default engines instead of the one-time autotune")
     ap.add_argument("--cpu-budget", type=float, default=10.0,
                     help="seconds of CPU oracle work for cpu_baseline (0 = skip)")
+    ap.add_argument("--crossover", action="store_true",
+                    help="time split LoRA against merged weights over a range of T and exit")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
                     help="only copy MIB MiB device-to-device (known-size kernel for scaling "
                          "the FETCH_SIZE / WRITE_SIZE counters) and exit")
@@ -198,6 +282,9 @@ def main():
             b.copy_(a)
         torch.cuda.synchronize()
         print(json.dumps({"calibrate_copy_bytes": n * 4, "copies": 3}))
+        return
+    if args.crossover:
+        crossover(args)
         return
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:

@@ -215,6 +215,30 @@ moe_status moe_lora_backward(const moe_dims* dims, const moe_bf16* dy, const moe
                              float* db_down, float* d_topk_w, float* d_logits, void* ws,
                              size_t ws_bytes, void* stream);
 
+/* The merged-weight path the pages compare split LoRA against (faster-MoE
+ * page, "Faster LoRA MoE training": PEFT merges the adapter into the base
+ * weight; "MoE LoRA changes things": split LoRA wins until the token count s
+ * passes a crossover, E m n / (k (m + n)) (1 + 1/(2r)) by the page's FLOP
+ * count).  Provided to measure that crossover on this GPU; the layer itself
+ * never merges.
+ * moe_merge_lora forms, for every one of the E_tot experts,
+ *   w_gate_up_merged[e] = W_gu[e] + s (A_gu[e] B_gu[e])^T    [E_tot, 2n, d]
+ *   w_down_merged[e]    = W_dn[e] + s (A_dn[e] B_dn[e])^T    [E_tot, d, n]
+ * with fp32 accumulation, rounded once to the element type.  The outputs are
+ * caller-owned device buffers of the weights' shapes; no workspace.
+ * moe_forward_merged is moe_lora_forward on such merged weights with the
+ * low-rank pass off (no X A / H A products): Y = combine(silu(gate) * up of
+ * X W'_gu^T, then H W'_dn^T).  saved and ws as for moe_lora_forward (the
+ * rank-r parts of saved are left unwritten, so it does not feed
+ * moe_lora_backward).  Its Y equals moe_lora_forward's to the layer's
+ * tolerance. */
+moe_status moe_merge_lora(const moe_dims* dims, const moe_weights* weights,
+                          moe_bf16* w_gate_up_merged, moe_bf16* w_down_merged, void* stream);
+moe_status moe_forward_merged(const moe_dims* dims, const moe_bf16* x, const moe_routing* routing,
+                              const moe_bf16* w_gate_up_merged, const moe_bf16* w_down_merged,
+                              moe_bf16* y, void* saved, size_t saved_bytes, void* ws,
+                              size_t ws_bytes, void* stream);
+
 /* Engines.  Every grouped product has two implementations: register-path
  * kernels (global -> registers -> LDS) and streamed ones (global -> LDS by
  * buffer_load ... lds through a ring, one persistent workgroup per CU).  Which

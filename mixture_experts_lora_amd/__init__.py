@@ -14,6 +14,7 @@ from .api import (  # noqa: F401
     ENGINE_RANK,
     Dims,
     Grads,
+    MergedWeights,
     MoELoRALayer,
     RouterGrads,
     Routing,
@@ -24,8 +25,10 @@ from .api import (  # noqa: F401
     empty_router_grads,
     empty_routing,
     forward,
+    forward_merged,
     forward_saved_bytes,
     get_engines,
+    merge_lora,
     route,
     route_noalloc,
     route_workspace_bytes,

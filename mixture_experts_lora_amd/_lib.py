@@ -27,6 +27,8 @@ EXPORTED = (
     "moe_route_noalloc",
     "moe_lora_forward",
     "moe_lora_backward",
+    "moe_merge_lora",
+    "moe_forward_merged",
     "moe_set_engines",
     "moe_get_engines",
     "moe_autotune_scratch_bytes",
@@ -89,6 +91,10 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.moe_lora_forward.argtypes = [pd, vp, pr, pw, vp, vp, sz, vp, sz, vp]
     lib.moe_lora_backward.restype = ctypes.c_int
     lib.moe_lora_backward.argtypes = [pd, vp, vp, pr, pw, vp, sz, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
+    lib.moe_merge_lora.restype = ctypes.c_int
+    lib.moe_merge_lora.argtypes = [pd, pw, vp, vp, vp]
+    lib.moe_forward_merged.restype = ctypes.c_int
+    lib.moe_forward_merged.argtypes = [pd, vp, pr, vp, vp, vp, vp, sz, vp, sz, vp]
     lib.moe_set_engines.restype = ctypes.c_int
     lib.moe_set_engines.argtypes = [pd, ctypes.c_uint]
     lib.moe_get_engines.restype = ctypes.c_uint

@@ -288,6 +288,53 @@ def backward(dy: torch.Tensor, x: torch.Tensor, routing: Routing, weights: Weigh
     return out
 
 
+class MergedWeights(NamedTuple):
+    """Base weights with the LoRA delta merged in (the path split LoRA avoids)."""
+    w_gate_up: torch.Tensor  # [E_tot, 2n, d]
+    w_down: torch.Tensor     # [E_tot, d, n]
+
+
+def merge_lora(weights: Weights, dims: Dims, out: Optional[MergedWeights] = None,
+               stream=None) -> MergedWeights:
+    """moe_merge_lora: W + s (A B)^T of every expert, both modules."""
+    lib = _lib.load()
+    _check_weights(weights, dims)
+    with _on(stream) as s:
+        if out is None:
+            out = MergedWeights(torch.empty_like(weights.w_gate_up), torch.empty_like(weights.w_down))
+        _check(out.w_gate_up, tuple(weights.w_gate_up.shape), dims.elem, "w_gate_up_merged")
+        _check(out.w_down, tuple(weights.w_down.shape), dims.elem, "w_down_merged")
+        dc, wc = dims.c(), _c_weights(weights)
+        _lib.check(lib.moe_merge_lora(ctypes.byref(dc), ctypes.byref(wc), out.w_gate_up.data_ptr(),
+                                      out.w_down.data_ptr(), s), "moe_merge_lora")
+    return out
+
+
+def forward_merged(x: torch.Tensor, routing: Routing, merged: MergedWeights, dims: Dims,
+                   y: Optional[torch.Tensor] = None, saved: Optional[torch.Tensor] = None,
+                   ws: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+    """moe_forward_merged: the forward on merged weights, low-rank pass off."""
+    lib = _lib.load()
+    Et, d, n = dims.E_tot, dims.d, dims.n
+    _check(x, (dims.T, d), dims.elem, "x")
+    _check_routing(routing, dims)
+    _check(merged.w_gate_up, (Et, 2 * n, d), dims.elem, "w_gate_up_merged")
+    _check(merged.w_down, (Et, d, n), dims.elem, "w_down_merged")
+    with _on(stream) as s:
+        y = y if y is not None else torch.empty_like(x)
+        _check(y, (dims.T, d), dims.elem, "y")
+        if saved is None:
+            saved = _bytes(forward_saved_bytes(dims), x.device)
+        if ws is None:
+            ws = _bytes(workspace_bytes(dims), x.device)
+        dc, rc = dims.c(), _c_routing(routing)
+        _lib.check(lib.moe_forward_merged(ctypes.byref(dc), x.data_ptr(), ctypes.byref(rc),
+                                          merged.w_gate_up.data_ptr(), merged.w_down.data_ptr(),
+                                          y.data_ptr(), saved.data_ptr(), saved.numel(),
+                                          ws.data_ptr(), ws.numel(), s), "moe_forward_merged")
+    return y
+
+
 ENGINE_GATE_UP, ENGINE_DOWN, ENGINE_DH, ENGINE_DX, ENGINE_RANK = 1, 2, 4, 8, 16
 ENGINE_ALL = 31
 

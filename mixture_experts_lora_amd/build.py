@@ -18,9 +18,9 @@ CSRC = os.path.join(PKG, "csrc")
 OBJ = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libmoe_lora.so")
 SOURCES = ("api.hip", "route.hip", "route_noalloc.hip", "gemm.hip", "stream.hip", "prepass.hip",
-           "grads.hip", "combine.hip", "layer.hip", "tune.hip", "timing.hip")
+           "grads.hip", "combine.hip", "merge.hip", "layer.hip", "tune.hip", "timing.hip")
 # compiled a second time with fp16 elements (-DMOE_F16, objects *_f16.o)
-ELEMENT_SOURCES = ("gemm.hip", "stream.hip", "prepass.hip", "grads.hip", "combine.hip")
+ELEMENT_SOURCES = ("gemm.hip", "stream.hip", "prepass.hip", "grads.hip", "combine.hip", "merge.hip")
 ARCH = "gfx950"
 
 HIPCC_FLAGS = [

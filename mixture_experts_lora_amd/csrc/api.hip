@@ -51,6 +51,7 @@ Layer make_layer(const moe_dims* dm) {
   L.s = dm->lora_scale;
   L.ncu = device_cu_count();
   L.f16 = dm->dtype == MOE_F16;
+  L.lora = 1;
   L.engines = lookup_engines(dm->d, dm->n, dm->E, dm->k, dm->r, dm->n_shared, L.f16);
   return L;
 }
@@ -188,6 +189,49 @@ moe_status moe_lora_forward(const moe_dims* dm, const moe_bf16* x, const moe_rou
   L.y = y;
   hipError_t e = maybe_pack(L, w, s);
   if (e == hipSuccess) e = EL(L, gemm_gate_up, L, s);
+  if (e == hipSuccess) e = EL(L, gemm_down, L, s);
+  if (e == hipSuccess) e = EL(L, launch_combine, L, true, L.o, L.y, s);
+  return launched(e);
+}
+
+moe_status moe_merge_lora(const moe_dims* dm, const moe_weights* w, moe_bf16* w_gate_up_merged,
+                          moe_bf16* w_down_merged, void* stream) {
+  moe_status st = check_dims(dm);
+  if (st != MOE_SUCCESS) return st;
+  if ((st = check_weights(w)) != MOE_SUCCESS) return st;
+  if (!aligned16(w_gate_up_merged) || !aligned16(w_down_merged)) return MOE_ERROR_INVALID_VALUE;
+  Layer L = make_layer(dm);
+  L.w_gu = w->w_gate_up;
+  L.w_dn = w->w_down;
+  L.b_gu = w->b_gate_up;
+  L.b_dn = w->b_down;
+  return launched(EL(L, merge_lora, L, w->a_gate_up, w->a_down, w_gate_up_merged, w_down_merged,
+                     (hipStream_t)stream));
+}
+
+moe_status moe_forward_merged(const moe_dims* dm, const moe_bf16* x, const moe_routing* rt,
+                              const moe_bf16* w_gate_up_merged, const moe_bf16* w_down_merged,
+                              moe_bf16* y, void* saved, size_t saved_bytes, void* ws,
+                              size_t ws_bytes, void* stream) {
+  moe_status st = check_dims(dm);
+  if (st != MOE_SUCCESS) return st;
+  if ((st = check_routing_in(rt)) != MOE_SUCCESS) return st;
+  if (!aligned16(x) || !aligned16(y) || !aligned16(saved) || !aligned16(ws) ||
+      !aligned16(w_gate_up_merged) || !aligned16(w_down_merged))
+    return MOE_ERROR_INVALID_VALUE;
+  if (saved_bytes < moe_forward_saved_bytes(dm) || ws_bytes < moe_workspace_bytes(dm))
+    return MOE_ERROR_WORKSPACE;
+  hipStream_t s = (hipStream_t)stream;
+  // the low-rank factor slots are never read with the low-rank pass off
+  const moe_weights mw = {w_gate_up_merged, w_down_merged, w_gate_up_merged, w_gate_up_merged,
+                          w_down_merged, w_down_merged};
+  Layer L = make_layer(dm);
+  L.lora = 0;
+  attach_common(L, rt, &mw, dm, ws);
+  attach_saved(L, dm, saved);
+  L.x = x;
+  L.y = y;
+  hipError_t e = EL(L, gemm_gate_up, L, s);
   if (e == hipSuccess) e = EL(L, gemm_down, L, s);
   if (e == hipSuccess) e = EL(L, launch_combine, L, true, L.o, L.y, s);
   return launched(e);

@@ -1141,6 +1141,8 @@ static void launch_prepass(const Layer& L, hipStream_t st, const char* name) {
 
 hipError_t gemm_gate_up(const Layer& L, hipStream_t st) {
   using C = MainCfg<MOE_CFG_GU>::type;
+  // on merged weights: the streamed product without its low-rank pass
+  if (!L.lora) return stream_gate_up(L, st);
   launch_prepass<PRE_XA>(L, st, "prepass_xa");
   if (L.engines & ENG_GU_STREAM) return stream_gate_up(L, st);
   const int tiles = mtiles_bound(L, C::BM) * cdiv(L.n, C::BN / 2);
@@ -1151,6 +1153,7 @@ hipError_t gemm_gate_up(const Layer& L, hipStream_t st) {
 
 hipError_t gemm_down(const Layer& L, hipStream_t st) {
   using C = MainCfg<MOE_CFG_DN>::type;
+  if (!L.lora) return stream_down(L, st);
   launch_prepass<PRE_HA>(L, st, "prepass_ha");
   if (L.engines & ENG_DN_STREAM) return stream_down(L, st);
   const int tiles = mtiles_bound(L, C::BM) * cdiv(L.d, C::BN);

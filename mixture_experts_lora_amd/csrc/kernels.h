@@ -35,6 +35,7 @@ enum EngineBits : uint32_t {
 struct Layer {
   int T, d, n, E, k, r, S, Et;
   int f16;           // elements are fp16 (else bf16)
+  int lora;          // the split low-rank pass runs (0: forward on merged weights)
   uint32_t engines;  // EngineBits
   int rs;       // row stride of the rank-r activations (r rounded up to 8)
   int ra;       // row stride used to read A_gu / A_dn (r, or rs for the packed copies)
@@ -130,6 +131,9 @@ enum PrepassKind { PRE_XA = 0, PRE_HA = 1, PRE_QDN = 2, PRE_QGU = 3 };
   hipError_t stream_prepass(const Layer& L, int kind, hipStream_t st);                            \
   /* LDS-DMA LoRA gradients, rank <= 64 (grads.hip) */                                            \
   hipError_t dma_lora_grads(const Layer& L, hipStream_t st);                                      \
+  /* W + s (A B)^T of every expert, both modules (merge.hip) */                                   \
+  hipError_t merge_lora(const Layer& L, const bf16_t* a_gu, const bf16_t* a_dn, bf16_t* w_gu_out,   \
+                        bf16_t* w_dn_out, hipStream_t st);                                          \
   /* weighted gather-combine of per-pair rows into token rows (combine.hip) */                   \
   hipError_t launch_combine(const Layer& L, bool weighted, const bf16_t* src, bf16_t* dst,        \
                             hipStream_t st);

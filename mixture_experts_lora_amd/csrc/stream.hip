@@ -189,13 +189,13 @@ struct SIssue {
   int step, smain, stot, rot;
 };
 
-template <int KIND>
+template <int KIND, bool LORA>
 __device__ __forceinline__ void s_setup(const Layer& L, const STile& T, const int* tok, SIssue& S) {
   const int n = L.n, d = L.d, rs = L.rs, ra = L.ra, r = L.r;
   const int lcm = s_lcm();
   const int e = T.e, row0 = T.row0, mrows = T.mrows;
   S.smain = s_kmain<KIND>(L) / SK;
-  S.stot = S.smain + cdiv(rs, SK);
+  S.stot = S.smain + (LORA ? cdiv(rs, SK) : 0);
   S.step = 0;
   // Each tile starts its base K loop 64 e k into the contraction of its
   // expert e (wrapping round; 128 bytes of a row per expert, at either stage
@@ -610,7 +610,10 @@ __device__ __forceinline__ void s_epilogue(const Layer& L, const STile& T, f32x1
     }
 }
 
-template <int KIND>
+// LORA: the rank-r steps follow each tile's base steps (the split LoRA
+// term); without them the kernel is the plain grouped GEMM, as the forward on
+// merged weights uses it.
+template <int KIND, bool LORA>
 __global__ __launch_bounds__(SNT) __attribute__((amdgpu_waves_per_eu(SNW / 4, SNW / 4))) void k_stream(const Layer L) {
   __shared__ __attribute__((aligned(1024))) bf16_t ring[SNS * SSTAGE];
   __shared__ __attribute__((aligned(16))) int tokbuf[2][TOKB];
@@ -642,7 +645,7 @@ __global__ __launch_bounds__(SNT) __attribute__((amdgpu_waves_per_eu(SNW / 4, SN
     __syncthreads();
   }
   SIssue S;
-  s_setup<KIND>(L, ti, tokbuf[0], S);
+  s_setup<KIND, LORA>(L, ti, tokbuf[0], S);
   int iord = 0;        // ordinal of the issue tile among this workgroup's tiles
   bool idone = false;  // no tile left to issue: repeat the last step
   // gather indices of the following tile, a whole tile ahead (wave 0, before
@@ -669,7 +672,7 @@ __global__ __launch_bounds__(SNT) __attribute__((amdgpu_waves_per_eu(SNW / 4, SN
       if (!idone && tn < total) {
         ++iord;
         ti = s_decode(pre, segst, Et, tn, ntn, nfull);
-        s_setup<KIND>(L, ti, tokbuf[iord & 1], S);
+        s_setup<KIND, LORA>(L, ti, tokbuf[iord & 1], S);
         issue_tok(tn + G, (iord + 1) & 1);
         // no scalar load of the switch stays pending into the step loop
         // (they return out of order, so a pending one would make every
@@ -695,7 +698,7 @@ __global__ __launch_bounds__(SNT) __attribute__((amdgpu_waves_per_eu(SNW / 4, SN
   // then the second half's MFMAs run while the next stage's first half is
   // read.
   const int smain = s_kmain<KIND>(L) / SK;
-  const int stot = smain + cdiv(rs, SK);
+  const int stot = smain + (LORA ? cdiv(rs, SK) : 0);
   int gc = 0;
   // The wait of step k: the stage after it must be in.  Younger than that
   // stage are the two issued after it, and in the first two steps of every
@@ -749,19 +752,26 @@ __global__ __launch_bounds__(SNT) __attribute__((amdgpu_waves_per_eu(SNW / 4, SN
     };
     using BM = std::integral_constant<bool, MN_M>;
     using BL = std::integral_constant<bool, MN_L>;
-#pragma unroll 1
-    for (int k = 0; k < smain - 1; ++k) step(BM{}, BM{}, k);
-    step(BM{}, BL{}, smain - 1);
-#pragma unroll 1
-    for (int k = smain; k < stot - 1; ++k) step(BL{}, BL{}, k);
-    {
+    // the last step of the tile: its remaining halves, no refill
+    auto last = [&](auto mn_cur) {
 #pragma unroll
-      for (int kk = 1; kk < HK; ++kk) s_mfma_read<MN_L>(f, acc, ring + (gc % SNS) * SSTAGE, kk);
+      for (int kk = 1; kk < HK; ++kk)
+        s_mfma_read<decltype(mn_cur)::value>(f, acc, ring + (gc % SNS) * SSTAGE, kk);
       ring_wait(stot - 1);
       wait_lgkm0();
       __syncthreads();
       s_mfma(f, acc);
       ++gc;
+    };
+#pragma unroll 1
+    for (int k = 0; k < smain - 1; ++k) step(BM{}, BM{}, k);
+    if constexpr (LORA) {
+      step(BM{}, BL{}, smain - 1);
+#pragma unroll 1
+      for (int k = smain; k < stot - 1; ++k) step(BL{}, BL{}, k);
+      last(BL{});
+    } else {
+      last(BM{});
     }
     // the stage read last is not refilled until every wave has staged its
     // outputs through it
@@ -781,20 +791,27 @@ __global__ __launch_bounds__(SNT) __attribute__((amdgpu_waves_per_eu(SNW / 4, SN
 
 }  // namespace
 
-template <int KIND>
+template <int KIND, bool LORA>
 static hipError_t launch_stream(const Layer& L, hipStream_t st, const char* name) {
   const int ntn = KIND == SK_GU ? cdiv(L.n, SBN / 2) : KIND == SK_DH ? cdiv(L.n, SBN) : cdiv(L.d, SBN);
   const int64_t tiles = (int64_t)(L.Ptot / SBM + L.Et) * ntn;
   int g = (int)std::min<int64_t>(tiles, L.ncu);
   g = std::max((g + 7) & ~7, 8);
-  MOE_LAUNCH(name, k_stream<KIND>, dim3(g), dim3(SNT), 0, st, L);
+  MOE_LAUNCH(name, (k_stream<KIND, LORA>), dim3(g), dim3(SNT), 0, st, L);
   return hipGetLastError();
 }
 
-hipError_t stream_gate_up(const Layer& L, hipStream_t st) { return launch_stream<SK_GU>(L, st, "gate_up"); }
-hipError_t stream_down(const Layer& L, hipStream_t st) { return launch_stream<SK_DN>(L, st, "down"); }
-hipError_t stream_dx(const Layer& L, hipStream_t st) { return launch_stream<SK_DX>(L, st, "dx"); }
-hipError_t stream_dh(const Layer& L, hipStream_t st) { return launch_stream<SK_DH>(L, st, "dh"); }
+// the forward products also run without the low-rank pass, on merged weights
+hipError_t stream_gate_up(const Layer& L, hipStream_t st) {
+  return L.lora ? launch_stream<SK_GU, true>(L, st, "gate_up")
+                : launch_stream<SK_GU, false>(L, st, "gate_up_merged");
+}
+hipError_t stream_down(const Layer& L, hipStream_t st) {
+  return L.lora ? launch_stream<SK_DN, true>(L, st, "down")
+                : launch_stream<SK_DN, false>(L, st, "down_merged");
+}
+hipError_t stream_dx(const Layer& L, hipStream_t st) { return launch_stream<SK_DX, true>(L, st, "dx"); }
+hipError_t stream_dh(const Layer& L, hipStream_t st) { return launch_stream<SK_DH, true>(L, st, "dh"); }
 
 }  // inline namespace MOE_EL
 }  // namespace moe

@@ -75,6 +75,7 @@ __all__ = [
     "forward",
     "forward_naive",
     "forward_merged",
+    "merged_weights",
     "forward_tokens",
     "backward",
     "backward_tokens",
@@ -319,22 +320,31 @@ def forward_naive(inp, topk_ids, topk_w, dims, dtype=np.float64):
     return y
 
 
+def merged_weights(inp, dims, dtype=np.float64):
+    """The merged weights PEFT forms [MOE]: per expert e,
+    W'_gu[e] = W_gu[e] + s (A_gu[e] B_gu[e])^T  ([2n, d]) and
+    W'_dn[e] = W_dn[e] + s (A_dn[e] B_dn[e])^T  ([d, n])."""
+    s = dims.lora_scale
+    W = _params(inp, dtype)
+    wgu = W["w_gu"] + s * np.transpose(W["a_gu"] @ W["b_gu"], (0, 2, 1))
+    wdn = W["w_dn"] + s * np.transpose(W["a_dn"] @ W["b_dn"], (0, 2, 1))
+    return wgu, wdn
+
+
 def forward_merged(inp, topk_ids, topk_w, dims, dtype=np.float64):
     """Forward on merged weights W' = W + s (A B)^T -- the path split LoRA
     avoids.  Identical to ``forward`` in exact arithmetic [MOE]."""
     T, d, n, E = dims.T, dims.d, dims.n, dims.E
-    s = dims.lora_scale
-    W = _params(inp, dtype)
     X = decode(inp, "x", dtype)
     w = np.asarray(topk_w, dtype=np.float32).astype(dtype)
+    WGU, WDN = merged_weights(inp, dims, dtype)
     y = np.zeros((T, d), dtype)
     for e, (tok, slot) in enumerate(route_naive(topk_ids, dims.E_tot)):
         if e >= E:
             tok, slot = np.arange(T), None
         if tok.size == 0:
             continue
-        wgu = W["w_gu"][e] + s * (W["a_gu"][e] @ W["b_gu"][e]).T
-        wdn = W["w_dn"][e] + s * (W["a_dn"][e] @ W["b_dn"][e]).T
+        wgu, wdn = WGU[e], WDN[e]
         g = X[tok] @ wgu.T
         h = silu(g[:, :n]) * g[:, n:]
         o = h @ wdn.T

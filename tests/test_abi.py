@@ -188,3 +188,25 @@ def test_engine_table_on_the_host(lib):
                             ctypes.byref(out)) == 3
     assert lib.moe_autotune(ctypes.byref(dm), 256, 256, 256, ctypes.byref(w), 128, need, None,
                             ctypes.byref(out)) == 1
+
+
+def test_merged_path_validates_on_the_host(lib):
+    dm = _dims()
+    fake = 4096
+    w = _lib.MoeWeights(*([fake] * 6))
+    rt = _lib.MoeRouting(*([fake] * 8))
+    assert lib.moe_merge_lora(None, ctypes.byref(w), fake, fake, None) == 1
+    assert lib.moe_merge_lora(ctypes.byref(dm), ctypes.byref(w), fake + 2, fake, None) == 1
+    assert lib.moe_merge_lora(ctypes.byref(dm), ctypes.byref(w), fake, None, None) == 1
+    bad_w = _lib.MoeWeights(fake, fake, fake, fake + 8, fake, fake)
+    assert lib.moe_merge_lora(ctypes.byref(dm), ctypes.byref(bad_w), fake, fake, None) == 1
+    dbad = _dims(d=96)
+    assert lib.moe_merge_lora(ctypes.byref(dbad), ctypes.byref(w), fake, fake, None) == 2
+    saved = lib.moe_forward_saved_bytes(ctypes.byref(dm))
+    ws = lib.moe_workspace_bytes(ctypes.byref(dm))
+    assert lib.moe_forward_merged(ctypes.byref(dm), fake, ctypes.byref(rt), fake, fake, fake, fake,
+                                  saved, fake, ws - 1, None) == 3
+    assert lib.moe_forward_merged(ctypes.byref(dm), fake, ctypes.byref(rt), fake, fake + 4, fake, fake,
+                                  saved, fake, ws, None) == 1
+    assert lib.moe_forward_merged(ctypes.byref(dbad), fake, ctypes.byref(rt), fake, fake, fake, fake,
+                                  saved, fake, ws, None) == 2
