@@ -429,11 +429,7 @@ def main():
         "kernels_us": {k: round(v, 2) for k, v in sorted(avg_us.items())},
         "memory_bound_kernels": mem,
         "router_grads": router,
-        "engines": {"bits": engines, "autotuned": not args.no_autotune,
-                    **{name: "streamed" if engines & bit else "register-path" for name, bit in
-                       (("gate_up", mel.ENGINE_GATE_UP), ("down", mel.ENGINE_DOWN),
-                        ("dh", mel.ENGINE_DH), ("dx", mel.ENGINE_DX),
-                        ("rank_r", mel.ENGINE_RANK))}},
+        "engines": {"bits": engines, "autotuned": not args.no_autotune, **mel.describe_engines(engines)},
     }
     if args.cpu_budget > 0:
         out["cpu_baseline"] = cpu_baseline(c, inp, args.cpu_budget)

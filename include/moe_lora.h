@@ -239,35 +239,52 @@ moe_status moe_forward_merged(const moe_dims* dims, const moe_bf16* x, const moe
                               moe_bf16* y, void* saved, size_t saved_bytes, void* ws,
                               size_t ws_bytes, void* stream);
 
-/* Engines.  Every grouped product has two implementations: register-path
- * kernels (global -> registers -> LDS) and streamed ones (global -> LDS by
- * buffer_load ... lds through a ring, one persistent workgroup per CU).  Which
- * runs is chosen per layer shape (d, n, E, k, r, n_shared; not T), process-
- * wide (and per element type), by these bits (set = streamed):
- *   MOE_ENGINE_GATE_UP, MOE_ENGINE_DOWN, MOE_ENGINE_DH, MOE_ENGINE_DX  the
- *     four grouped GEMMs;
- *   MOE_ENGINE_RANK  the rank-r pre-passes and the LoRA gradients (r <= 64;
- *     above that both settings use the register path).
- * Without a recorded choice a shape uses the build's defaults (everything
- * streamed).
- * moe_set_engines records a choice (MOE_ERROR_INVALID_VALUE for unknown bits);
- * moe_get_engines returns the choice in force.  Results agree between engines
- * to the layer's tolerance, not bitwise.
+/* Engines and tile configurations.  Every grouped product has two
+ * implementations: register-path kernels (global -> registers -> LDS) and
+ * streamed ones (global -> LDS by buffer_load ... lds through a ring, one
+ * persistent workgroup per CU), the streamed ones in four tile
+ * configurations.  What runs is chosen per layer shape (d, n, E, k, r,
+ * n_shared; not T), process-wide (and per element type), by these bits:
+ *   MOE_ENGINE_GATE_UP, _DOWN, _DH, _DX (bits 0-3)  set = streamed grouped
+ *     GEMM for that product;
+ *   MOE_ENGINE_RANK (bit 4)  set = streamed rank-r pre-passes and LoRA
+ *     gradients (r <= 64; above that both settings use the register path);
+ *   MOE_TILE256(p) (bits 5-8)  set = 256-row tiles for product p (0 gate_up,
+ *     1 down, 2 dh, 3 dx), else 320 rows;
+ *   MOE_STAGE32(p) (bits 9-12)  set = ring stages of 32 k for product p, else
+ *     64 k (tile bits matter only when the product is streamed);
+ *   MOE_SPLITK_1024, MOE_SPLITK_4096 (bits 13-14, one value)  rows per split-K
+ *     chunk of the LoRA gradients, else 2048.
+ * Without a recorded choice a shape uses MOE_ENGINE_DEFAULT (everything
+ * streamed, 320-row tiles, 64-k stages, 2048-row chunks).
+ * moe_set_engines records a choice (MOE_ERROR_INVALID_VALUE for unknown bits
+ * or split-K field 3); moe_get_engines returns the choice in force.  Results
+ * agree between settings to the layer's tolerance, not bitwise.
  * moe_autotune is the one-time start-up autotune of the faster-MoE page's
  * kernels ("Unsloth MoE Triton kernels"), cached per shape: it runs route +
- * forward + backward on the given inputs under each setting (all streamed, all
- * register-path), twice in alternation (one warm-up and three timed steps
- * each time, every kernel timed with events), keeps per product the engine
- * with the lower of its two times, records and returns the choice.  Unlike every other entry point it waits for the GPU; it also
- * switches the kernel-timing recorder off.  scratch: device memory of at
- * least moe_autotune_scratch_bytes(dims), 256-byte aligned, for all the
- * routing, saved, workspace and output buffers of those steps; its contents
- * are undefined afterwards.  logits, x, dy, weights as for the other calls. */
+ * forward + backward on the given inputs under seven settings (streamed with
+ * each of the four tile configurations, register path, streamed with
+ * 1024- and 4096-row split-K chunks), twice in alternation (one warm-up and
+ * three timed steps each time, every kernel timed with events), and picks per
+ * product the setting with the lowest time -- another setting than the
+ * default only when it is more than 1 % faster -- then records and returns
+ * the combined choice.  Unlike every other entry point it waits for the GPU;
+ * it uses (and leaves switched off) the calling thread's kernel-timing
+ * recorder, so autotunes on different threads do not interfere.  scratch:
+ * device memory of at least moe_autotune_scratch_bytes(dims), 256-byte
+ * aligned, for all the routing, saved, workspace and output buffers of those
+ * steps; its contents are undefined afterwards.  logits, x, dy, weights as
+ * for the other calls. */
 #define MOE_ENGINE_GATE_UP 1u
 #define MOE_ENGINE_DOWN 2u
 #define MOE_ENGINE_DH 4u
 #define MOE_ENGINE_DX 8u
 #define MOE_ENGINE_RANK 16u
+#define MOE_ENGINE_DEFAULT 31u
+#define MOE_TILE256(p) (1u << (5 + (p)))
+#define MOE_STAGE32(p) (1u << (9 + (p)))
+#define MOE_SPLITK_1024 (1u << 13)
+#define MOE_SPLITK_4096 (2u << 13)
 moe_status moe_set_engines(const moe_dims* dims, unsigned engines);
 unsigned moe_get_engines(const moe_dims* dims);
 size_t moe_autotune_scratch_bytes(const moe_dims* dims);
@@ -277,11 +294,11 @@ moe_status moe_autotune(const moe_dims* dims, const float* logits, const moe_bf1
 
 /* Kernel timing, for measurement tools (not part of the layer's math).
  * moe_timing_enable(1) starts recording: every kernel the library enqueues
- * afterwards is bracketed by two HIP events on its stream (a few
- * microseconds of extra gaps per kernel).  moe_timing_enable(0) stops
- * recording.  Both clear previous records.  Recording is process-wide and not
- * thread-safe; the first enable creates the event pool (host call, no device
- * memory).  Returns MOE_ERROR_LAUNCH if events cannot be created.
+ * afterwards from the calling host thread is bracketed by two HIP events on
+ * its stream (a few microseconds of extra gaps per kernel).
+ * moe_timing_enable(0) stops recording.  Both clear previous records.  Each
+ * host thread has its own recorder; a thread's first enable creates its
+ * event pool (host call, no device memory).  Returns MOE_ERROR_LAUNCH if events cannot be created.
  * moe_timing_report waits for the recorded events, then writes up to
  * max_entries distinct kernel names (each NUL-terminated in a name_len-byte
  * slot of `names`), the summed milliseconds and the launch count per name,

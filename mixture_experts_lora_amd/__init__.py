@@ -12,6 +12,11 @@ from .api import (  # noqa: F401
     ENGINE_DX,
     ENGINE_GATE_UP,
     ENGINE_RANK,
+    PRODUCTS,
+    SPLITK_1024,
+    SPLITK_4096,
+    STAGE32,
+    TILE256,
     Dims,
     Grads,
     MergedWeights,
@@ -21,6 +26,7 @@ from .api import (  # noqa: F401
     Weights,
     autotune,
     backward,
+    describe_engines,
     empty_grads,
     empty_router_grads,
     empty_routing,

@@ -336,7 +336,34 @@ def forward_merged(x: torch.Tensor, routing: Routing, merged: MergedWeights, dim
 
 
 ENGINE_GATE_UP, ENGINE_DOWN, ENGINE_DH, ENGINE_DX, ENGINE_RANK = 1, 2, 4, 8, 16
-ENGINE_ALL = 31
+ENGINE_ALL = 31          # every product streamed, default tiles (MOE_ENGINE_DEFAULT)
+PRODUCTS = ("gate_up", "down", "dh", "dx")
+SPLITK_1024, SPLITK_4096 = 1 << 13, 2 << 13
+
+
+def TILE256(p: int) -> int:
+    """Engine bit: 256-row tiles (else 320) for product p (0 gate_up, 1 down, 2 dh, 3 dx)."""
+    return 1 << (5 + p)
+
+
+def STAGE32(p: int) -> int:
+    """Engine bit: 32-k ring stages (else 64-k) for product p."""
+    return 1 << (9 + p)
+
+
+def describe_engines(bits: int) -> dict:
+    """Readable form of an engine/tile word."""
+    out = {}
+    for p, name in enumerate(PRODUCTS):
+        if bits & (1 << p):
+            out[name] = (f"streamed {256 if bits & TILE256(p) else 320}x256 "
+                         f"{32 if bits & STAGE32(p) else 64}-k")
+        else:
+            out[name] = "register-path"
+    f = (bits >> 13) & 3
+    out["rank_r"] = ("streamed" if bits & ENGINE_RANK else "register-path") + \
+        f", split-K {({0: 2048, 1: 1024, 2: 4096}).get(f, '?')} rows"
+    return out
 
 
 def set_engines(dims: Dims, engines: int) -> None:

@@ -17,10 +17,13 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 OBJ = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libmoe_lora.so")
-SOURCES = ("api.hip", "route.hip", "route_noalloc.hip", "gemm.hip", "stream.hip", "prepass.hip",
+SOURCES = ("api.hip", "route.hip", "route_noalloc.hip", "gemm.hip", "prepass.hip",
            "grads.hip", "combine.hip", "merge.hip", "layer.hip", "tune.hip", "timing.hip")
 # compiled a second time with fp16 elements (-DMOE_F16, objects *_f16.o)
-ELEMENT_SOURCES = ("gemm.hip", "stream.hip", "prepass.hip", "grads.hip", "combine.hip", "merge.hip")
+ELEMENT_SOURCES = ("gemm.hip", "prepass.hip", "grads.hip", "combine.hip", "merge.hip")
+# the streamed grouped GEMM, once per tile height x stage depth (namespace,
+# rows, k per stage), each with bf16 and with fp16 elements
+STREAM_TILES = (("t320k64", 320, 64), ("t256k64", 256, 64), ("t320k32", 320, 32), ("t256k32", 256, 32))
 ARCH = "gfx950"
 
 HIPCC_FLAGS = [
@@ -61,6 +64,9 @@ def build(extra_flags: list[str] | None = None, verbose: bool = True, out: str =
     OBJ = objdir
     os.makedirs(OBJ, exist_ok=True)
     jobs = [(s, extra, "") for s in SOURCES] + [(s, extra + ["-DMOE_F16"], "_f16") for s in ELEMENT_SOURCES]
+    for ns, bm, sk in STREAM_TILES:
+        tile = [f"-DMOE_STILE={ns}", f"-DMOE_SBM={bm}", f"-DMOE_SK={sk}"]
+        jobs += [("stream.hip", extra + tile, f"_{ns}"), ("stream.hip", extra + tile + ["-DMOE_F16"], f"_{ns}_f16")]
     with cf.ThreadPoolExecutor(max_workers=min(len(jobs), 16)) as ex:
         objs = list(ex.map(lambda j: _compile(*j), jobs))
     tmp = out + ".tmp"

@@ -53,6 +53,7 @@ Layer make_layer(const moe_dims* dm) {
   L.f16 = dm->dtype == MOE_F16;
   L.lora = 1;
   L.engines = lookup_engines(dm->d, dm->n, dm->E, dm->k, dm->r, dm->n_shared, L.f16);
+  L.splitk = splitk_rows(L.engines);
   return L;
 }
 

@@ -979,7 +979,7 @@ __global__ __launch_bounds__(C::NT) __attribute__((amdgpu_waves_per_eu(C::OCC)))
 // out[e] (M x N, fp32) = sum over expert e's rows p of U(p, m) V(p, c); the
 // LoRA scale s is already inside the rank-r rows (s X A_gu, s H A_dn, Q_dn,
 // Q_gu).  Both operands are read with the row index p as contraction index.  A chunk
-// of at most SPLITK_ROWS rows makes one partial; an expert with a single
+// of at most L.splitk rows makes one partial; an expert with a single
 // chunk writes its result directly, otherwise into its partial slot for the
 // fixed-order reduction.
 enum GradKind { GR_DB_DN = 0, GR_DA_DN = 1, GR_DB_GU = 2, GR_DA_GU = 3 };
@@ -990,7 +990,7 @@ __global__ __launch_bounds__(C::NT) __attribute__((amdgpu_waves_per_eu(C::OCC)))
   __shared__ __attribute__((aligned(16))) bf16_t lds[C::LDS_ELEMS];
   __shared__ int pre[MAX_ET + 1];
   __shared__ int sh[C::NW];
-  expert_prefix<NT>(L, pre, sh, [&](int e) { return cdiv(seg_count(L, e), SPLITK_ROWS); });
+  expert_prefix<NT>(L, pre, sh, [&](int e) { return cdiv(seg_count(L, e), L.splitk); });
   const int n = L.n, d = L.d, rs = L.rs;
   int M, N;
   grad_shape(KIND, d, n, L.r, M, N);
@@ -1008,8 +1008,8 @@ __global__ __launch_bounds__(C::NT) __attribute__((amdgpu_waves_per_eu(C::OCC)))
     const int e = find_expert(pre, L.Et, slot, 1);
     const int chunk = slot - pre[e];
     const int nchunk = pre[e + 1] - pre[e];
-    const int kb = seg_start(L, e) + chunk * SPLITK_ROWS;
-    const int kn = min(seg_count(L, e) - chunk * SPLITK_ROWS, SPLITK_ROWS);
+    const int kb = seg_start(L, e) + chunk * L.splitk;
+    const int kn = min(seg_count(L, e) - chunk * L.splitk, L.splitk);
     const int m0 = mt * BM, c0 = nt * BN;
     const int nk = cdiv(kn, BK);
     const bool act = wave_active<C>(M - m0, N - c0);
@@ -1078,7 +1078,7 @@ __global__ __launch_bounds__(RED_NT) void k_grad_reduce(const Layer L) {
   // first partial slot of every expert (chunks of the experts before it)
   __shared__ int pre[MAX_ET + 1];
   __shared__ int sh[RED_NT / 64];
-  expert_prefix<RED_NT>(L, pre, sh, [&](int e) { return cdiv(seg_count(L, e), SPLITK_ROWS); });
+  expert_prefix<RED_NT>(L, pre, sh, [&](int e) { return cdiv(seg_count(L, e), L.splitk); });
   // usually every expert has exactly one chunk: then nothing is left to do
   int need = 0;
   for (int e = threadIdx.x; e < L.Et; e += RED_NT) need |= pre[e + 1] - pre[e] != 1;
@@ -1139,6 +1139,27 @@ static void launch_prepass(const Layer& L, hipStream_t st, const char* name) {
   }
 }
 
+// The streamed products in the tile configuration the layer's engine bits
+// give each one (product p: 0 gate_up, 1 down, 2 dh, 3 dx): bit 5 + p =
+// 256-row tiles, bit 9 + p = 32-k ring stages.
+static int tile_cfg(const Layer& L, int p) {
+  return (int)((L.engines >> (5 + p)) & 1u) | (int)(((L.engines >> (9 + p)) & 1u) << 1);
+}
+#define MOE_STREAM_DISPATCH(fn, p)                       \
+  hipError_t fn(const Layer& L, hipStream_t st) {        \
+    switch (tile_cfg(L, p)) {                            \
+      case 1: return t256k64::fn(L, st);                 \
+      case 2: return t320k32::fn(L, st);                 \
+      case 3: return t256k32::fn(L, st);                 \
+      default: return t320k64::fn(L, st);                \
+    }                                                    \
+  }
+MOE_STREAM_DISPATCH(stream_gate_up, 0)
+MOE_STREAM_DISPATCH(stream_down, 1)
+MOE_STREAM_DISPATCH(stream_dh, 2)
+MOE_STREAM_DISPATCH(stream_dx, 3)
+#undef MOE_STREAM_DISPATCH
+
 hipError_t gemm_gate_up(const Layer& L, hipStream_t st) {
   using C = MainCfg<MOE_CFG_GU>::type;
   // on merged weights: the streamed product without its low-rank pass
@@ -1191,7 +1212,7 @@ template <class C, int KIND>
 static void launch_grad(const Layer& L, hipStream_t st, const char* name) {
   int M, N;
   grad_shape(KIND, L.d, L.n, L.r, M, N);
-  const int slots = L.Ptot / SPLITK_ROWS + L.Et;
+  const int slots = L.Ptot / L.splitk + L.Et;
   const int tiles = slots * cdiv(M, C::BM) * cdiv(N, C::BN);
   MOE_LAUNCH(name, (k_lora_grad<C, KIND>), dim3(grid_for(tiles, wg_per_cu<C>(), L.ncu)), dim3(C::NT),
              0, st, L);

@@ -15,7 +15,7 @@
 // consecutive rows of one column).  Token-gathered operands (dY, X) take their
 // row offsets from the segment chunk's gather indices, staged in LDS at tile
 // start.  Tiles are 64 (the rank side) x 256, 4 waves of 64 x 64, and the
-// four kinds share one persistent launch; segments longer than SPLITK_ROWS
+// four kinds share one persistent launch; segments longer than L.splitk
 // are split into chunks whose fp32 partials k_grad_reduce sums in chunk
 // order.
 #include <algorithm>
@@ -151,8 +151,8 @@ __device__ __forceinline__ void grad_tile(const Layer& L, int t, bf16_t* ring, i
   const int e = __builtin_amdgcn_readfirstlane(find_expert(pre, L.Et, slot, 1));
   const int chunk = __builtin_amdgcn_readfirstlane(slot - pre[e]);
   const int nchunk = __builtin_amdgcn_readfirstlane(pre[e + 1] - pre[e]);
-  const int kb = __builtin_amdgcn_readfirstlane(seg_start(L, e) + chunk * SPLITK_ROWS);
-  const int kn = __builtin_amdgcn_readfirstlane(min(seg_count(L, e) - chunk * SPLITK_ROWS, SPLITK_ROWS));
+  const int kb = __builtin_amdgcn_readfirstlane(seg_start(L, e) + chunk * L.splitk);
+  const int kn = __builtin_amdgcn_readfirstlane(min(seg_count(L, e) - chunk * L.splitk, L.splitk));
   const int m0 = mt * P::BM, c0 = nt * P::BN;
   if (P::U_GATHER || P::V_GATHER) {
     for (int i = threadIdx.x; i < kn; i += GNT) tokbuf[i] = L.tok[kb + i];
@@ -243,10 +243,10 @@ static_assert(GP<1>::STAGE == GSTAGE && GP<2>::STAGE == GSTAGE && GP<3>::STAGE =
 template <int K0>
 __global__ __launch_bounds__(GNT) __attribute__((amdgpu_waves_per_eu(2))) void k_grad_all(const Layer L) {
   __shared__ __attribute__((aligned(1024))) bf16_t ring[GNS * GSTAGE];
-  __shared__ __attribute__((aligned(16))) int tokbuf[SPLITK_ROWS];
+  __shared__ __attribute__((aligned(16))) int tokbuf[SPLITK_MAX];
   __shared__ int pre[MAX_ET + 1];
   __shared__ int sh[GNW];
-  expert_prefix<GNT>(L, pre, sh, [&](int e) { return cdiv(seg_count(L, e), SPLITK_ROWS); });
+  expert_prefix<GNT>(L, pre, sh, [&](int e) { return cdiv(seg_count(L, e), L.splitk); });
   const int slots = pre[L.Et];
   const int c1 = K0 <= 0 ? slots * grad_per_slot<0>(L) : 0;
   const int c2 = c1 + (K0 <= 1 ? slots * grad_per_slot<1>(L) : 0);
@@ -287,7 +287,7 @@ hipError_t dma_lora_grads(const Layer& L, hipStream_t st) {
     MOE_LAUNCH("weight_rows", k_weight_rows, dim3(g), dim3(256), 0, st, L, L.qdn, L.qw);
   }
   // upper bound of the merged tile list (slots per expert <= rows / chunk + 1)
-  const int64_t slots = L.Ptot / SPLITK_ROWS + L.Et;
+  const int64_t slots = L.Ptot / L.splitk + L.Et;
   int64_t tiles = 0;
   for (int kind = 0; kind < 4; ++kind) {
     int M, N;

@@ -29,8 +29,26 @@ enum EngineBits : uint32_t {
   ENG_DH_STREAM = 1u << 2,    // dh (+ SwiGLU backward); router-gradient partials need it
   ENG_DX_STREAM = 1u << 3,    // dX per pair
   ENG_RANK_STREAM = 1u << 4,  // rank-r pre-passes and LoRA gradients (rank <= 64)
-  ENG_ALL = 31u
+  ENG_ALL = 31u,
+  // tile configuration of each streamed product (product p = 0 gate_up,
+  // 1 down, 2 dh, 3 dx): bit 5 + p set = 256-row tiles (else 320), bit 9 + p
+  // set = 32-k ring stages (else 64-k)
+  ENG_TILE256 = 1u << 5,
+  ENG_STAGE32 = 1u << 9,
+  // rows per split-K chunk of the LoRA gradients: field value 0 = 2048,
+  // 1 = 1024, 2 = 4096
+  ENG_SPLITK_SHIFT = 13,
+  ENG_SPLITK_MASK = 3u << 13,
+  ENG_VALID = (1u << 15) - 1
 };
+constexpr int SPLITK_MIN = 1024, SPLITK_MAX = 4096;
+inline int splitk_rows(uint32_t engines) {
+  const uint32_t f = (engines & ENG_SPLITK_MASK) >> ENG_SPLITK_SHIFT;
+  return f == 1 ? 1024 : f == 2 ? 4096 : 2048;
+}
+inline bool engines_valid(uint32_t engines) {
+  return (engines & ~(uint32_t)ENG_VALID) == 0 && (engines & ENG_SPLITK_MASK) != ENG_SPLITK_MASK;
+}
 
 struct Layer {
   int T, d, n, E, k, r, S, Et;
@@ -40,6 +58,7 @@ struct Layer {
   int rs;       // row stride of the rank-r activations (r rounded up to 8)
   int ra;       // row stride used to read A_gu / A_dn (r, or rs for the packed copies)
   int P, Ptot;  // routed pairs, all rows
+  int splitk;   // rows per split-K chunk of the LoRA gradients (splitk_rows(engines))
   float s;      // LoRA scale
   int ncu;      // compute units of the device (persistent grid sizing)
   // routing
@@ -122,7 +141,8 @@ enum PrepassKind { PRE_XA = 0, PRE_HA = 1, PRE_QDN = 2, PRE_QGU = 3 };
   uint32_t default_engines(); /* the engines used when none was chosen for a shape */             \
   /* whether the Q_dn pre-pass also writes w Q_dn and w (s H A_dn) (the streamed one does) */     \
   bool prepass_writes_weighted_rows(const Layer& L);                                              \
-  /* streamed products without their pre-pass (stream.hip) */                                     \
+  /* streamed products without their pre-pass, in the tile configuration   */                    \
+  /* the layer's engine bits choose (gemm.hip, over the builds of stream.hip) */                   \
   hipError_t stream_gate_up(const Layer& L, hipStream_t st);                                      \
   hipError_t stream_down(const Layer& L, hipStream_t st);                                         \
   hipError_t stream_dx(const Layer& L, hipStream_t st);                                           \
@@ -138,16 +158,31 @@ enum PrepassKind { PRE_XA = 0, PRE_HA = 1, PRE_QDN = 2, PRE_QGU = 3 };
   hipError_t launch_combine(const Layer& L, bool weighted, const bf16_t* src, bf16_t* dst,        \
                             hipStream_t st);
 
+// stream.hip, built once per tile height x stage depth
+#define MOE_STREAM_LAUNCHERS                                    \
+  hipError_t stream_gate_up(const Layer& L, hipStream_t st);    \
+  hipError_t stream_down(const Layer& L, hipStream_t st);       \
+  hipError_t stream_dx(const Layer& L, hipStream_t st);         \
+  hipError_t stream_dh(const Layer& L, hipStream_t st);
+#define MOE_STREAM_TILES             \
+  namespace t320k64 { MOE_STREAM_LAUNCHERS } \
+  namespace t256k64 { MOE_STREAM_LAUNCHERS } \
+  namespace t320k32 { MOE_STREAM_LAUNCHERS } \
+  namespace t256k32 { MOE_STREAM_LAUNCHERS }
+
 inline namespace MOE_EL {
 MOE_ELEMENT_LAUNCHERS
+MOE_STREAM_TILES
 }
 #ifdef MOE_F16
 namespace el_bf16 {
 MOE_ELEMENT_LAUNCHERS
+MOE_STREAM_TILES
 }
 #else
 namespace el_f16 {
 MOE_ELEMENT_LAUNCHERS
+MOE_STREAM_TILES
 }
 #endif
 
@@ -172,7 +207,6 @@ void timing_post(hipStream_t st);
     ::moe::timing_post(stream);                                              \
   } while (0)
 
-constexpr int SPLITK_ROWS = 2048;  // segment rows per split-K chunk of the LoRA grads
 constexpr int PREPASS_MAX_SPLIT = 4;
 
 // Contraction splits of a rank-r pre-pass: enough row tiles x splits to give

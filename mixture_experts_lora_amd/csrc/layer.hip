@@ -24,7 +24,8 @@ WsLayout ws_layout(int64_t T, int d, int n, int E, int k, int r, int S) {
   w.hw = off;       off += align256((size_t)Ptot * rs * 2);
   w.qw = off;       off += align256((size_t)Ptot * rs * 2);
   w.dw_part = off;  off += align256((size_t)Ptot * (n / 64) * 4);
-  const int64_t slots = Ptot / SPLITK_ROWS + Et;
+  // partial slots for the smallest split-K chunk any engine setting uses
+  const int64_t slots = Ptot / SPLITK_MIN + Et;
   int64_t pf = 0;
   for (int kind = 0; kind < 4; ++kind) {
     int M, N;

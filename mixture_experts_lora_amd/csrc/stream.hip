@@ -49,12 +49,22 @@
 #include <algorithm>
 #include <type_traits>
 
+//
+// The tile height (MOE_SBM: 320 or 256 rows) and the stage depth (MOE_SK: 64
+// or 32 k) are build parameters: the library holds this file compiled once
+// per combination, each in its own namespace (MOE_STILE), and the per-shape
+// tile choice picks one per product.
 #include "common.h"
 #include "gemm_util.h"
 #include "kernels.h"
 
+#ifndef MOE_STILE
+#define MOE_STILE t320k64
+#endif
+
 namespace moe {
 inline namespace MOE_EL {
+namespace MOE_STILE {
 namespace {
 
 #ifndef MOE_SBM
@@ -554,14 +564,6 @@ __device__ __forceinline__ void s_epilogue_dh(const Layer& L, const STile& T, f3
   }
 }
 
-// Store instructions each wave issues in one tile's epilogue.
-template <int KIND>
-constexpr int s_epi_stores() {
-  // per fragment pair and readback row group: GU G and H; DH dgate, dup and
-  // the <dH, H> partial; else one
-  return SFM * (SFN / 2) * 4 * (KIND == SK_GU ? 2 : KIND == SK_DH ? 3 : 1);
-}
-
 template <int KIND>
 __device__ __forceinline__ void s_epilogue(const Layer& L, const STile& T, f32x16 (&acc)[SFM][SFN], bf16_t* wl) {
   static_assert(KIND != SK_DH, "dh has its own epilogue");
@@ -700,20 +702,17 @@ __global__ __launch_bounds__(SNT) __attribute__((amdgpu_waves_per_eu(SNW / 4, SN
   const int smain = s_kmain<KIND>(L) / SK;
   const int stot = smain + (LORA ? cdiv(rs, SK) : 0);
   int gc = 0;
-  // The wait of step k: the stage after it must be in.  Younger than that
-  // stage are the two issued after it, and in the first two steps of every
-  // tile but the first the previous tile's epilogue stores, issued between
-  // them (vector memory operations retire in issue order).
+  // The wait of step k: the stage after it must be in; younger than that
+  // stage are the SNS - 2 stages issued after it.  In the first two steps of
+  // every tile but the first, the previous tile's epilogue stores were issued
+  // in between: those waits are full (vmcnt 0), so they never count on how
+  // stores and loads retire relative to each other.
   constexpr int WAIT_HI = (SNS - 2) * PER_HI, WAIT_LO = (SNS - 2) * PER_LO;
-  constexpr int EPI = s_epi_stores<KIND>();
-  constexpr int WAIT_EPI_HI = SNS == 2 ? 0 : WAIT_HI + EPI < 63 ? WAIT_HI + EPI : 63;
-  constexpr int WAIT_EPI_LO = SNS == 2 ? 0 : WAIT_LO + EPI < 63 ? WAIT_LO + EPI : 63;
   const bool hi = A_REM == 0 || wid < A_REM;  // this wave issues PER_HI per stage
   bool after_epi = false;
   auto ring_wait = [&](int k) {
     if (after_epi && k < 2) {
-      if (hi) wait_vmcnt<WAIT_EPI_HI>();
-      else wait_vmcnt<WAIT_EPI_LO>();
+      wait_vmcnt<0>();
     } else {
       if (hi) wait_vmcnt<WAIT_HI>();
       else wait_vmcnt<WAIT_LO>();
@@ -813,5 +812,6 @@ hipError_t stream_down(const Layer& L, hipStream_t st) {
 hipError_t stream_dx(const Layer& L, hipStream_t st) { return launch_stream<SK_DX, true>(L, st, "dx"); }
 hipError_t stream_dh(const Layer& L, hipStream_t st) { return launch_stream<SK_DH, true>(L, st, "dh"); }
 
+}  // namespace MOE_STILE
 }  // inline namespace MOE_EL
 }  // namespace moe

@@ -1,10 +1,9 @@
 // Opt-in kernel timing: when enabled, every kernel the library launches is
 // bracketed by a pair of HIP events on its stream; the report sums the
-// elapsed times per kernel name.  Diagnostics only (off by default, one
-// process-wide recorder, not thread-safe while enabled).
+// elapsed times per kernel name.  Diagnostics only (off by default).  Each
+// host thread has its own recorder, so the autotune of one thread and the
+// calls of another do not mix their records.
 #include <string.h>
-
-#include <atomic>
 
 #include "../../include/moe_lora.h"
 #include "kernels.h"
@@ -13,23 +12,30 @@ namespace moe {
 
 namespace {
 constexpr int CAP = 8192;
-std::atomic<int> g_on{0};
-int g_used = 0;
-bool g_created = false;
-hipEvent_t g_start[CAP], g_stop[CAP];
-const char* g_name[CAP];
+struct Recorder {
+  int on = 0, used = 0;
+  bool created = false;
+  hipEvent_t start[CAP], stop[CAP];
+  const char* name[CAP];
+};
+// created on a thread's first enable (events and all), kept until exit
+thread_local Recorder* t_rec = nullptr;
 }  // namespace
 
 void timing_pre(const char* name, hipStream_t st) {
-  if (!g_on.load(std::memory_order_relaxed) || g_used >= CAP) return;
-  g_name[g_used] = name;
-  (void)hipEventRecord(g_start[g_used], st);
+  if (!t_rec) return;
+  Recorder& r = *t_rec;
+  if (!r.on || r.used >= CAP) return;
+  r.name[r.used] = name;
+  (void)hipEventRecord(r.start[r.used], st);
 }
 
 void timing_post(hipStream_t st) {
-  if (!g_on.load(std::memory_order_relaxed) || g_used >= CAP) return;
-  (void)hipEventRecord(g_stop[g_used], st);
-  ++g_used;
+  if (!t_rec) return;
+  Recorder& r = *t_rec;
+  if (!r.on || r.used >= CAP) return;
+  (void)hipEventRecord(r.stop[r.used], st);
+  ++r.used;
 }
 
 }  // namespace moe
@@ -39,29 +45,36 @@ using namespace moe;
 extern "C" {
 
 moe_status moe_timing_enable(int on) {
-  if (on && !g_created) {
+  if (!t_rec) {
+    if (!on) return MOE_SUCCESS;
+    t_rec = new Recorder();
+  }
+  Recorder& r = *t_rec;
+  if (on && !r.created) {
     for (int i = 0; i < CAP; ++i) {
-      if (hipEventCreate(&g_start[i]) != hipSuccess || hipEventCreate(&g_stop[i]) != hipSuccess)
+      if (hipEventCreate(&r.start[i]) != hipSuccess || hipEventCreate(&r.stop[i]) != hipSuccess)
         return MOE_ERROR_LAUNCH;
     }
-    g_created = true;
+    r.created = true;
   }
-  g_used = 0;
-  g_on.store(on ? 1 : 0, std::memory_order_relaxed);
+  r.used = 0;
+  r.on = on ? 1 : 0;
   return MOE_SUCCESS;
 }
 
 int moe_timing_report(char* names, int name_len, float* total_ms, int* launches, int max_entries) {
+  if (!t_rec) return 0;
+  Recorder& r = *t_rec;
   int n = 0;
-  for (int i = 0; i < g_used; ++i) {
+  for (int i = 0; i < r.used; ++i) {
     float ms = 0.f;
-    if (hipEventSynchronize(g_stop[i]) != hipSuccess) return -1;
-    if (hipEventElapsedTime(&ms, g_start[i], g_stop[i]) != hipSuccess) return -1;
+    if (hipEventSynchronize(r.stop[i]) != hipSuccess) return -1;
+    if (hipEventElapsedTime(&ms, r.start[i], r.stop[i]) != hipSuccess) return -1;
     int j = 0;
-    while (j < n && strncmp(names + (size_t)j * name_len, g_name[i], name_len) != 0) ++j;
+    while (j < n && strncmp(names + (size_t)j * name_len, r.name[i], name_len) != 0) ++j;
     if (j == n) {
       if (n >= max_entries) continue;
-      strncpy(names + (size_t)n * name_len, g_name[i], name_len - 1);
+      strncpy(names + (size_t)n * name_len, r.name[i], name_len - 1);
       names[(size_t)n * name_len + name_len - 1] = 0;
       total_ms[n] = 0.f;
       launches[n] = 0;
@@ -70,7 +83,7 @@ int moe_timing_report(char* names, int name_len, float* total_ms, int* launches,
     total_ms[j] += ms;
     launches[j] += 1;
   }
-  g_used = 0;
+  r.used = 0;
   return n;
 }
 

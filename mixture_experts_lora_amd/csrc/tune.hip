@@ -1,12 +1,16 @@
-// Engine choice per layer shape, and the one-time autotune that makes it
-// (the faster-MoE page's kernels pick their configurations by a start-up
-// autotune, "Unsloth MoE Triton kernels"; here the choice is between the two
-// engines every grouped product has: the register-path kernels of gemm.hip
-// and the streamed LDS-DMA kernels of stream.hip / prepass.hip / grads.hip).
+// Engine and tile choice per layer shape, and the one-time autotune that
+// makes it (the faster-MoE page's kernels pick their configurations by a
+// start-up autotune, "Unsloth MoE Triton kernels").  Per grouped product the
+// choice is the register-path kernel of gemm.hip or the streamed kernel of
+// stream.hip in one of its four tile configurations (320- or 256-row tiles,
+// 64- or 32-k ring stages); for the rank-r group (pre-passes and LoRA
+// gradients) the register path or the streamed one with 2048-, 1024- or
+// 4096-row split-K chunks.
 #include <string.h>
 
 #include <algorithm>
 #include <array>
+#include <initializer_list>
 #include <map>
 #include <mutex>
 
@@ -103,7 +107,7 @@ moe_status time_products(const moe_dims* dm, const float* logits, const moe_bf16
   if (st != MOE_SUCCESS) return st;
   if ((st = moe_timing_enable(1)) != MOE_SUCCESS) return st;
   for (int i = 0; i < STEPS && st == MOE_SUCCESS; ++i) st = run_layer(dm, logits, x, dy, w, b, stream);
-  static char names[MAXN * NAME];
+  char names[MAXN * NAME];  // per call: concurrent autotunes on other threads keep their own
   float ms[MAXN];
   int launches[MAXN];
   const int cnt = moe_timing_report(names, NAME, ms, launches, MAXN);
@@ -134,7 +138,7 @@ moe_status time_products(const moe_dims* dm, const float* logits, const moe_bf16
 extern "C" {
 
 moe_status moe_set_engines(const moe_dims* dm, unsigned engines) {
-  if (!dm || (engines & ~(unsigned)ENG_ALL)) return MOE_ERROR_INVALID_VALUE;
+  if (!dm || !engines_valid(engines)) return MOE_ERROR_INVALID_VALUE;
   record_engines(dm->d, dm->n, dm->E, dm->k, dm->r, dm->n_shared, dm->dtype == MOE_F16, engines);
   return MOE_SUCCESS;
 }
@@ -157,27 +161,49 @@ moe_status moe_autotune(const moe_dims* dm, const float* logits, const moe_bf16*
   if (scratch_bytes < moe_autotune_scratch_bytes(dm)) return MOE_ERROR_WORKSPACE;
   TuneBufs b = carve(dm, (char*)scratch);
   const unsigned before = moe_get_engines(dm);
+  // the settings timed: each sets every product alike; per product the
+  // fastest setting wins (a product's kernels do not depend on the others')
+  constexpr uint32_t ALL4 = 15u;  // the four products' bits of a tile field
+  constexpr int NSET = 7, REG = 4;
+  const uint32_t settings[NSET] = {
+      ENG_ALL,                                                 // 0: streamed, 320 rows, 64-k (default)
+      ENG_ALL | (ALL4 << 5),                                   // 1: 256-row tiles
+      ENG_ALL | (ALL4 << 9),                                   // 2: 32-k stages
+      ENG_ALL | (ALL4 << 5) | (ALL4 << 9),                     // 3: both
+      0u,                                                      // 4: register path
+      ENG_ALL | (1u << ENG_SPLITK_SHIFT),                      // 5: 1024-row split-K chunks
+      ENG_ALL | (2u << ENG_SPLITK_SHIFT)};                     // 6: 4096-row split-K chunks
   // each setting twice, alternating, best of the two per product: the first
   // timed runs of a process can be slower while the clocks settle
-  double ts[5], tr[5], t[5];
-  for (int i = 0; i < 5; ++i) ts[i] = tr[i] = 1e30;
+  double best[NSET][5], t[5];
+  for (auto& row : best)
+    for (double& v : row) v = 1e30;
   moe_status st = MOE_SUCCESS;
   for (int round = 0; round < 2 && st == MOE_SUCCESS; ++round)
-    for (int streamed = 1; streamed >= 0 && st == MOE_SUCCESS; --streamed) {
-      moe_set_engines(dm, streamed ? ENG_ALL : 0u);
+    for (int i = 0; i < NSET && st == MOE_SUCCESS; ++i) {
+      moe_set_engines(dm, settings[i]);
       st = time_products(dm, logits, x, dy, w, b, stream, t);
-      double* best = streamed ? ts : tr;
-      for (int i = 0; i < 5; ++i) best[i] = std::min(best[i], t[i]);
+      for (int p = 0; p < 5; ++p) best[i][p] = std::min(best[i][p], t[p]);
     }
   if (st != MOE_SUCCESS) {
     moe_set_engines(dm, before);
     return st;
   }
-  const uint32_t bits[5] = {ENG_GU_STREAM, ENG_DN_STREAM, ENG_DH_STREAM, ENG_DX_STREAM,
-                            ENG_RANK_STREAM};
+  // a setting other than the default has to win by more than 1 % (run-to-run
+  // noise is about that size)
+  auto pick = [&](int p, std::initializer_list<int> cands) {
+    int w = 0;
+    for (int i : cands)
+      if (best[i][p] < best[w][p] && best[i][p] < 0.99 * best[0][p]) w = i;
+    return w;
+  };
   unsigned chosen = 0;
-  for (int i = 0; i < 5; ++i)
-    if (ts[i] <= tr[i]) chosen |= bits[i];
+  for (int p = 0; p < 4; ++p) {
+    const int w = pick(p, {1, 2, 3, REG});
+    if (w != REG) chosen |= (1u << p) | (settings[w] & (((1u << 5) | (1u << 9)) << p));
+  }
+  const int wr = pick(4, {REG, 5, 6});
+  if (wr != REG) chosen |= ENG_RANK_STREAM | (settings[wr] & ENG_SPLITK_MASK);
   moe_set_engines(dm, chosen);
   if (engines_out) *engines_out = chosen;
   return MOE_SUCCESS;

@@ -170,8 +170,12 @@ def test_fp16_dims_accepted_and_keyed_apart(lib):
 def test_engine_table_on_the_host(lib):
     dm = _lib.MoeDims(T=64, d=128, n=64, E=8, k=2, r=4, n_shared=0, lora_scale=1.0)
     default = lib.moe_get_engines(ctypes.byref(dm))
-    assert 0 <= default <= 31
-    assert lib.moe_set_engines(ctypes.byref(dm), 32) == 1          # unknown bit
+    assert default == 31                                             # streamed, default tiles
+    assert lib.moe_set_engines(ctypes.byref(dm), 1 << 15) == 1      # unknown bit
+    assert lib.moe_set_engines(ctypes.byref(dm), 3 << 13) == 1      # split-K field 3 is not a value
+    tiles = 31 | (1 << 5) | (1 << 10) | (2 << 13)                    # 256-row gate_up, 32-k down, 4096 chunks
+    assert lib.moe_set_engines(ctypes.byref(dm), tiles) == 0
+    assert lib.moe_get_engines(ctypes.byref(dm)) == tiles
     assert lib.moe_set_engines(ctypes.byref(dm), 5) == 0
     assert lib.moe_get_engines(ctypes.byref(dm)) == 5
     other = _lib.MoeDims(T=64, d=128, n=64, E=8, k=2, r=8, n_shared=0, lora_scale=1.0)

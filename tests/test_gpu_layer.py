@@ -96,10 +96,27 @@ ENGINE_CASES = ["tiny", "ragged_shared_r3_s2", "r128_n192", "empty_experts_r64",
                 "wide_d320_zipf_f16"]
 
 
-@pytest.mark.parametrize("engines", [0, mel.ENGINE_ALL], ids=["register_path", "streamed"])
+ALL4 = sum(1 << p for p in range(4))
+SETTINGS = {
+    "register_path": 0,
+    "streamed": mel.ENGINE_ALL,
+    "streamed_256rows": mel.ENGINE_ALL | (ALL4 << 5),
+    "streamed_32k": mel.ENGINE_ALL | (ALL4 << 9),
+    "streamed_256rows_32k": mel.ENGINE_ALL | (ALL4 << 5) | (ALL4 << 9),
+    "splitk_1024": mel.ENGINE_ALL | mel.SPLITK_1024,
+    "splitk_4096": mel.ENGINE_ALL | mel.SPLITK_4096,
+    "mixed": (mel.ENGINE_ALL & ~mel.ENGINE_DOWN) | mel.TILE256(0) | mel.STAGE32(2) | mel.TILE256(3)
+             | mel.STAGE32(3) | mel.SPLITK_1024,
+}
+
+
+@pytest.mark.parametrize("engines", list(SETTINGS.values()), ids=list(SETTINGS))
 @pytest.mark.parametrize("name", ENGINE_CASES)
 def test_layer_parity_each_engine(name, engines):
-    """Every product on one engine: all register-path kernels, or all streamed."""
+    """Every product under one setting the autotune can choose: all
+    register-path kernels, all streamed in each tile configuration (320 or
+    256 rows, 64- or 32-k stages), each split-K chunk of the LoRA gradients,
+    and one mixed setting."""
     require_gpu()
     ld = CASES[name]
     announce("engines", f"{name} engines={engines}", ld)
@@ -137,7 +154,8 @@ def test_autotune_records_a_choice_that_keeps_parity():
     try:
         chosen = mel.autotune(dims, logits, x, dy, w)
         print("chosen engines", chosen, flush=True)
-        assert 0 <= chosen <= mel.ENGINE_ALL
+        print(mel.describe_engines(chosen), flush=True)
+        assert chosen & ~0x7FFF == 0 and (chosen >> 13) & 3 != 3  # a valid engine/tile word
         assert mel.get_engines(dims) == chosen
         rt, y, g, rg = _run(dims, logits, x, dy, w)
     finally:
