@@ -18,9 +18,15 @@ Prints ONE JSON line.  Besides the standard benchmark fields it carries
                 the router, so they are not part of the step): a third timed
                 region of backward calls that also produce them, its extra
                 time per step and the router_grad kernel against HBM peak;
-  engines       the engine of each product (the one-time autotune's choice,
-                made before the warm-up steps, unless --no-autotune);
-  cpu_baseline  the CPU oracle timed on a bounded sample of the same workload.
+  engines       the engine and tile configuration of each product (the
+                one-time autotune's choice, made before the warm-up steps,
+                unless --no-autotune);
+  cpu_baseline  the CPU oracle timed on a bounded sample of the same workload;
+  configs       the other workloads (tiny, deepseek_shared, long_zipf,
+                routing_stress, and the headline shape with fp16 elements),
+                each autotuned and timed for ms/step, tokens/s, TFLOP/s, step
+                roofline fraction and grouped-GEMM fraction of the bf16 peak,
+                next to its time under the build's default engines.
 """
 from __future__ import annotations
 
@@ -230,6 +236,85 @@ def crossover(args):
     print(json.dumps(out), flush=True)
 
 
+# the workloads besides the headline one, each measured in the same run
+OTHER_CONFIGS = (("tiny", "bf16"), ("deepseek_shared", "bf16"), ("long_zipf", "bf16"),
+                 ("routing_stress", "bf16"), ("qwen3_30b_a3b", "f16"))
+
+
+def measure_config(name: str, dtype: str, steps: int, warmup: int) -> dict:
+    """One workload: the one-time autotune, then route + forward + backward
+    steps under the build's default engines and under the autotuned ones
+    (HIP events around each timed region), and one event-timed pass of the
+    autotuned steps for the per-kernel figures."""
+    import numpy as np
+    import torch
+
+    import mixture_experts_lora_amd as mel
+    from mixture_experts_lora_amd import _lib
+    from synth import CONFIGS, make_inputs
+
+    c = dataclasses.replace(CONFIGS[name], element=dtype)
+    inp = make_inputs(c, seed=0)
+    dims = mel.Dims(c.T, c.d, c.n, c.E, c.k, c.r, c.n_shared, c.lora_scale,
+                    mel.MOE_F16 if dtype == "f16" else mel.MOE_BF16)
+
+    def up(a):
+        return torch.from_numpy(a.view(np.int16)).cuda().view(dims.elem)
+
+    w = mel.Weights(up(inp.w_gu), up(inp.w_dn), up(inp.a_gu), up(inp.b_gu), up(inp.a_dn), up(inp.b_dn))
+    logits = torch.from_numpy(inp.logits).cuda()
+    x, dy = up(inp.x), up(inp.dy)
+    layer = mel.MoELoRALayer(dims, w)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+
+    def step():
+        layer.route(logits)
+        layer.forward(x)
+        layer.backward(dy, x)
+
+    def timed():
+        for _ in range(warmup):
+            step()
+        torch.cuda.synchronize()
+        e0.record()
+        for _ in range(steps):
+            step()
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / steps
+
+    chosen = mel.autotune(dims, logits, x, dy, w)
+    mel.set_engines(dims, mel.ENGINE_ALL)
+    default_ms = timed()
+    mel.set_engines(dims, chosen)
+    ms = timed()
+    _lib.timing_enable(True)
+    for _ in range(steps):
+        step()
+    torch.cuda.synchronize()
+    rep = _lib.timing_report()
+    _lib.timing_enable(False)
+    work = kernel_work(c)
+    gemm_flops = sum(work[k][0] for k in GEMM_KERNELS if k in rep)
+    gemm_time = sum(rep[k][0] for k in GEMM_KERNELS if k in rep) / steps * 1e-3
+    gu_us = 1e3 * rep["gate_up"][0] / rep["gate_up"][1]
+    roof = step_roofline(c, ms)
+    out = {"T": c.T, "d": c.d, "n": c.n, "E": c.E, "top_k": c.k, "lora_rank": c.r,
+           "n_shared": c.n_shared, "logits": c.logits_recipe, "dtype": dtype,
+           "ms_per_step": round(ms, 4), "default_engines_ms_per_step": round(default_ms, 4),
+           "tokens_per_s": round(c.T / (ms * 1e-3), 1),
+           "tflop_s": round(roof["algorithmic_flops"] / (ms * 1e-3) / 1e12, 1),
+           "step_roofline": {k: roof[k] for k in ("bound", "t_roof_us", "frac")},
+           "gemm_mfma_frac": round(gemm_flops / gemm_time / PEAK_BF16, 4),
+           "gemm_tflops": round(gemm_flops / gemm_time / 1e12, 1),
+           "gate_up": {"us": round(gu_us, 2), "tflop_s": round(work["gate_up"][0] / gu_us / 1e6, 1),
+                       "GB/s": round(work["gate_up"][1] / gu_us / 1e3, 1)},
+           "engines": {"bits": chosen, **mel.describe_engines(chosen)}}
+    del layer, w, x, dy, logits
+    torch.cuda.empty_cache()
+    return out
+
+
 def measured_traffic(kernel: str, workload: str):
     """HBM bytes per launch of `kernel` from the committed rocprofv3 counter
     summary, or None when the kernel source changed since it was measured."""
@@ -265,6 +350,8 @@ def main():
                     help="keep the build's default engines instead of the one-time autotune")
     ap.add_argument("--cpu-budget", type=float, default=10.0,
                     help="seconds of CPU oracle work for cpu_baseline (0 = skip)")
+    ap.add_argument("--no-configs", action="store_true",
+                    help="measure only the headline workload (skip the `configs` object)")
     ap.add_argument("--crossover", action="store_true",
                     help="time split LoRA against merged weights over a range of T and exit")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
@@ -433,6 +520,16 @@ def main():
     }
     if args.cpu_budget > 0:
         out["cpu_baseline"] = cpu_baseline(c, inp, args.cpu_budget)
+    if not args.no_configs:
+        del layer, w, x, dy, logits
+        torch.cuda.empty_cache()
+        out["configs"] = {}
+        for name, dt in OTHER_CONFIGS:
+            if (name, dt) == (args.config, args.dtype):
+                continue
+            key = name if dt == "bf16" else f"{name}_{dt}"
+            out["configs"][key] = measure_config(name, dt, min(args.steps, 10), min(args.warmup, 3))
+            print(f"[bench] {key}: {out['configs'][key]['ms_per_step']} ms/step", file=sys.stderr, flush=True)
     print(json.dumps(out), flush=True)
 
 
