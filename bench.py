@@ -315,9 +315,10 @@ def measure_config(name: str, dtype: str, steps: int, warmup: int) -> dict:
     return out
 
 
-def measured_traffic(kernel: str, workload: str):
-    """HBM bytes per launch of `kernel` from the committed rocprofv3 counter
-    summary, or None when the kernel source changed since it was measured."""
+def measured_traffic(kernel: str, workload: str, tile: str):
+    """HBM bytes per launch of `kernel` in tile configuration `tile` (e.g.
+    t320k64) from the committed rocprofv3 counter summary, or None when that
+    configuration was not measured or the kernel source changed since."""
     import hashlib
     import re
 
@@ -326,7 +327,7 @@ def measured_traffic(kernel: str, workload: str):
         return None
     text = open(path).read()
     m_sha = re.search(r"source_sha256:\s*([0-9a-f]{64})", text)
-    m_b = re.search(r"traffic_bytes_per_launch:\s*([0-9]+)", text)
+    m_b = re.search(r"traffic_bytes_per_launch\[" + tile + r"\]:\s*([0-9]+)", text)
     m_src = re.search(r"source_files:\s*(.+)", text)
     if not (m_sha and m_b and m_src):
         return None
@@ -348,6 +349,8 @@ def main():
                     help="16-bit element type of activations and weights")
     ap.add_argument("--no-autotune", action="store_true",
                     help="keep the build's default engines instead of the one-time autotune")
+    ap.add_argument("--engines", type=int, default=None, metavar="BITS",
+                    help="use this engine/tile word instead of the autotune (for profiling)")
     ap.add_argument("--cpu-budget", type=float, default=10.0,
                     help="seconds of CPU oracle work for cpu_baseline (0 = skip)")
     ap.add_argument("--no-configs", action="store_true",
@@ -406,7 +409,11 @@ def main():
     layer = mel.MoELoRALayer(dims, w)
     # one-time per-shape engine autotune before any timed step (untimed, as
     # the start-up autotune of the pages' kernels)
-    engines = mel.get_engines(dims) if args.no_autotune else mel.autotune(dims, logits, x, dy, w)
+    if args.engines is not None:
+        mel.set_engines(dims, args.engines)
+        engines = args.engines
+    else:
+        engines = mel.get_engines(dims) if args.no_autotune else mel.autotune(dims, logits, x, dy, w)
 
     def step():
         layer.route(logits)
@@ -448,8 +455,11 @@ def main():
         roof = {"bound": "mfma", "achieved": f / t_dom / 1e12, "peak": PEAK_BF16 / 1e12,
                 "unit": "TFLOP/s"}
     roof["frac"] = roof["achieved"] / roof["peak"]
-    roof["traffic"] = measured_traffic(dom, args.config if args.dtype == "bf16"
-                                       else f"{args.config}_{args.dtype}")
+    gu_tile = f"t{256 if engines & mel.TILE256(0) else 320}k{32 if engines & mel.STAGE32(0) else 64}"
+    roof["traffic"] = (measured_traffic(dom, args.config if args.dtype == "bf16"
+                                        else f"{args.config}_{args.dtype}", gu_tile)
+                       if engines & mel.ENGINE_GATE_UP else None)
+    roof["tile"] = gu_tile
     roof["kernel"] = dom
     roof["kernel_us"] = avg_us[dom]
     roof["algorithmic_bytes"] = byts
@@ -516,7 +526,8 @@ def main():
         "kernels_us": {k: round(v, 2) for k, v in sorted(avg_us.items())},
         "memory_bound_kernels": mem,
         "router_grads": router,
-        "engines": {"bits": engines, "autotuned": not args.no_autotune, **mel.describe_engines(engines)},
+        "engines": {"bits": engines, "autotuned": not args.no_autotune and args.engines is None,
+                    **mel.describe_engines(engines)},
     }
     if args.cpu_budget > 0:
         out["cpu_baseline"] = cpu_baseline(c, inp, args.cpu_budget)
