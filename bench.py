@@ -22,6 +22,8 @@ Prints ONE JSON line.  Besides the standard benchmark fields it carries
                 one-time autotune's choice, made before the warm-up steps,
                 unless --no-autotune);
   cpu_baseline  the CPU oracle timed on a bounded sample of the same workload;
+  cpu_naive_loop  the oracle's per-expert search loop (the pages' starting
+                point), forward only, float64, timed the same way, as context;
   configs       the other workloads (tiny, deepseek_shared, long_zipf,
                 routing_stress, and the headline shape with fp16 elements),
                 each autotuned and timed for ms/step, tokens/s, TFLOP/s, step
@@ -298,6 +300,13 @@ def measure_config(name: str, dtype: str, steps: int, warmup: int) -> dict:
     gemm_flops = sum(work[k][0] for k in GEMM_KERNELS if k in rep)
     gemm_time = sum(rep[k][0] for k in GEMM_KERNELS if k in rep) / steps * 1e-3
     gu_us = 1e3 * rep["gate_up"][0] / rep["gate_up"][1]
+    avg_us = {k: 1e3 * v[0] / v[1] for k, v in rep.items()}
+    route_us = sum(avg_us.get(k, 0.0) for k in ("route_select", "route_scatter"))
+    mem = {"route": {"us": round(route_us, 2), "GB/s": round(work["route"][1] / route_us / 1e3, 1)}}
+    for k in ("combine_y", "combine_dx"):
+        mem[k] = {"us": round(avg_us[k], 2), "GB/s": round(work[k][1] / avg_us[k] / 1e3, 1)}
+    for v in mem.values():
+        v["frac_of_hbm_peak"] = round(v["GB/s"] * 1e9 / PEAK_HBM, 3)
     roof = step_roofline(c, ms)
     out = {"T": c.T, "d": c.d, "n": c.n, "E": c.E, "top_k": c.k, "lora_rank": c.r,
            "n_shared": c.n_shared, "logits": c.logits_recipe, "dtype": dtype,
@@ -309,10 +318,40 @@ def measure_config(name: str, dtype: str, steps: int, warmup: int) -> dict:
            "gemm_tflops": round(gemm_flops / gemm_time / 1e12, 1),
            "gate_up": {"us": round(gu_us, 2), "tflop_s": round(work["gate_up"][0] / gu_us / 1e6, 1),
                        "GB/s": round(work["gate_up"][1] / gu_us / 1e3, 1)},
+           "memory_bound_kernels": mem,
            "engines": {"bits": chosen, **mel.describe_engines(chosen)}}
     del layer, w, x, dy, logits
     torch.cuda.empty_cache()
     return out
+
+
+def cpu_naive_loop(dims, inp, budget_s: float):
+    """The per-expert search loop the pages start from (oracle.forward_naive:
+    every expert finds its tokens with a data-dependent query, runs its MLP on
+    them and adds the weighted result), float64 numpy, forward only, on the
+    first T_s tokens (T_s grows until one pass takes about budget_s / 3);
+    context beside cpu_baseline, not a target."""
+    import statistics
+
+    import numpy as np
+    import oracle
+
+    def one(Ts):
+        sd = dataclasses.replace(dims, T=Ts)
+        sub = dataclasses.replace(inp, dims=sd, logits=inp.logits[:Ts], x=inp.x[:Ts], dy=inp.dy[:Ts])
+        t0 = time.perf_counter()
+        ids, w = oracle.topk_softmax(sub.logits, sd.k)
+        oracle.forward_naive(sub, ids, w, sd, dtype=np.float64)
+        return time.perf_counter() - t0
+
+    Ts = 64
+    dt = one(Ts)
+    while dt < budget_s / 3 and Ts < dims.T:
+        Ts = min(dims.T, max(Ts * 2, int(Ts * budget_s / 3 / max(dt, 1e-3))))
+        dt = one(Ts)
+    med = statistics.median([dt, one(Ts), one(Ts)])
+    return {"value": Ts / med, "unit": "tokens/s (forward only)", "kind": "oracle per-expert loop, float64",
+            "sample": f"first {Ts} of {dims.T} tokens, route + forward, median of 3 passes = {med:.2f} s"}
 
 
 def measured_traffic(kernel: str, workload: str, tile: str):
@@ -531,6 +570,7 @@ def main():
     }
     if args.cpu_budget > 0:
         out["cpu_baseline"] = cpu_baseline(c, inp, args.cpu_budget)
+        out["cpu_naive_loop"] = cpu_naive_loop(c, inp, min(args.cpu_budget, 6.0))
     if not args.no_configs:
         del layer, w, x, dy, logits
         torch.cuda.empty_cache()
