@@ -1,9 +1,10 @@
 """Forward and backward on the GPU against the float64 oracle, element by
 element, at sizes the oracle finishes in seconds: several M/N tiles, ragged
-segment tails, ranks that are and are not multiples of 8, a shared expert, a
-LoRA scale other than 1, empty experts, split-K LoRA gradients, k = E, k = 1,
-T = 1, the largest expert count (256 with the shared one); the routing-weight and logit gradients with every case; every case
-again with fp16 elements.
+segment tails, ranks that are and are not multiples of 8 (rank 1 included), a
+shared expert, LoRA scales of 2, 0 and -0.75, empty experts, split-K LoRA
+gradients, k = E, k = 1, T = 1, a single expert, the largest expert count (256
+with the shared one); the routing-weight and logit gradients with every case;
+every case again with fp16 elements.
 
 Every reference is the oracle's, from the oracle's own routing (its top-k ids,
 which the GPU's must equal bit for bit, and its routing weights, which the
@@ -39,6 +40,13 @@ CASES = {
     "prepass_splits": LayerDims(200, 1024, 256, 4, 2, 16),
     # the most experts the library takes: 255 routed + 1 shared = 256, most of them empty or tiny
     "max_experts_255_shared": LayerDims(600, 64, 64, 255, 4, 8, n_shared=1),
+    # rank 1: one column of each adapter
+    "rank_one": LayerDims(150, 64, 128, 4, 2, 1),
+    # one expert, k = 1: every token's weight is 1, the layer is one dense SwiGLU MLP with LoRA
+    "single_expert": LayerDims(130, 128, 64, 1, 1, 8),
+    # LoRA scale 0: only the base path is left and every LoRA gradient is exactly zero
+    "scale_zero": LayerDims(100, 64, 64, 4, 2, 8, lora_scale=0.0),
+    "scale_negative_shared": LayerDims(90, 64, 64, 3, 2, 5, n_shared=1, lora_scale=-0.75),
 }
 CASES.update({f"{k}_f16": replace(v, element="f16") for k, v in list(CASES.items())})
 
@@ -83,6 +91,10 @@ def test_layer_parity(name):
     for e in np.nonzero(counts == 0)[0]:
         for key in ("da_gu", "db_gu", "da_dn", "db_dn"):
             assert not np.any(to_numpy_f64(got[key])[e]), (key, e)
+    # with LoRA scale 0 every adapter gradient is a sum of products with a zero factor
+    if ld.lora_scale == 0:
+        for key in ("da_gu", "db_gu", "da_dn", "db_dn"):
+            assert not np.any(to_numpy_f64(got[key])), key
     # bitwise reproducible
     rt2, y2, g2, rg2 = _run(dims, logits, x, dy, w)
     assert torch.equal(y.view(torch.int16), y2.view(torch.int16))
