@@ -516,6 +516,32 @@ def main():
     for v in mem.values():
         v["frac_of_hbm_peak"] = round(v["GB/s"] * 1e9 / PEAK_HBM, 3)
 
+    # the same step captured once as a HIP graph and replayed: the kernels and
+    # their work are unchanged, the host launch gaps between them are gone
+    def graph_ms():
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):
+            step()
+        torch.cuda.current_stream().wait_stream(side)
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            step()
+        for _ in range(2):
+            g.replay()
+        torch.cuda.synchronize()
+        t0.record()
+        for _ in range(args.steps):
+            g.replay()
+        t1.record()
+        torch.cuda.synchronize()
+        del g
+        return t0.elapsed_time(t1) / args.steps
+
+    g_ms = graph_ms()
+    graph = {"ms_per_step": round(g_ms, 4), "tokens_per_s": round(c.T / (g_ms * 1e-3), 1)}
+
     # optional router gradients: backward alone, without and with them
     def bwd_ms(router):
         for _ in range(2):
@@ -564,6 +590,7 @@ def main():
         "step_roofline": step_roofline(c, ms),
         "kernels_us": {k: round(v, 2) for k, v in sorted(avg_us.items())},
         "memory_bound_kernels": mem,
+        "graph_replay": graph,
         "router_grads": router,
         "engines": {"bits": engines, "autotuned": not args.no_autotune and args.engines is None,
                     **mel.describe_engines(engines)},
