@@ -129,11 +129,31 @@ def cpu_baseline(dims, inp, budget_s: float):
     import numpy as np
     import oracle
 
+    # BLAS threads: threadpoolctl when it recognises numpy's BLAS, else the
+    # variables OpenBLAS reads, else every core
+    env_threads = os.environ.get("OPENBLAS_NUM_THREADS") or os.environ.get("OMP_NUM_THREADS")
+    threads = int(env_threads) if env_threads and env_threads.isdigit() else os.cpu_count()
     try:
         from threadpoolctl import threadpool_info
-        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [os.cpu_count()])
+        found = [i.get("num_threads", 1) for i in threadpool_info() if i.get("user_api") == "blas"]
+        if found:
+            threads = max(found)
     except Exception:  # pragma: no cover
-        threads = os.cpu_count()
+        pass
+    try:
+        blas = np.show_config(mode="dicts")["Build Dependencies"]["blas"]
+        blas = f"{blas.get('name', '?')} {blas.get('version', '')}".strip()
+    except Exception:  # pragma: no cover
+        blas = "unknown"
+    cpu = "unknown"
+    try:
+        with open("/proc/cpuinfo") as fh:
+            for line in fh:
+                if line.startswith("model name"):
+                    cpu = line.split(":", 1)[1].strip()
+                    break
+    except OSError:  # pragma: no cover
+        pass
 
     def one(Ts):
         sd = dataclasses.replace(dims, T=Ts)
@@ -153,7 +173,8 @@ def cpu_baseline(dims, inp, budget_s: float):
     med = statistics.median([dt, one(Ts), one(Ts)])
     return {"value": Ts / med, "unit": "tokens/s", "cores": int(threads), "kind": "oracle",
             "sample": f"first {Ts} of {dims.T} tokens (same seeded inputs), float32 numpy "
-                      f"route+forward+backward, median of 3 passes = {med:.2f} s"}
+                      f"route+forward+backward, median of 3 passes = {med:.2f} s",
+            "blas": blas, "host_cpu": cpu, "host_cpus": os.cpu_count()}
 
 
 CROSSOVER_T = (1024, 2048, 4096, 8192, 12288, 16384, 24576, 32768, 49152)
