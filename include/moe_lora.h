@@ -40,7 +40,11 @@
  *  - Outputs are overwritten, never accumulated into (an expert that receives
  *    no rows gets exactly zero LoRA gradients).
  *  - Work is enqueued asynchronously on `stream` (a hipStream_t; NULL = the
- *    default stream).  No call synchronises the host or copies to the host.
+ *    default stream).  No call synchronises the host or copies to the host,
+ *    except moe_autotune and moe_timing_report, which wait for their own
+ *    work.  The other calls allocate nothing, enqueue no memset and never
+ *    wait, so they can be captured into a HIP graph; a replay reuses the
+ *    pointers and sizes given at capture.
  *  - The return code covers host-side validation and launch errors only; on
  *    any error nothing has been enqueued except in the MOE_ERROR_LAUNCH case.
  *  - Device-side data errors (an expert id outside [0, E) in a routing
