@@ -105,6 +105,26 @@ def test_hand_worked_example():
         assert not np.any(bw[key][0])  # expert 0 received nothing
 
 
+@pytest.mark.parametrize("s", [1.0, 2.0])
+def test_hand_merged_weights(s):
+    """W' = W + s (A B)^T written out for the hand example's experts."""
+    inp = _hand_inputs()
+    dims = replace(inp.dims, lora_scale=s)
+    wgu, wdn = oracle.merged_weights(replace(inp, dims=dims), dims)
+    # expert 1: A_gu B_gu = [[0.5, -0.25], [0.5, -0.25]] ([d, 2n]); its
+    # transpose is added to W_gu [[1, 0.5], [0.25, 1]] ([2n, d])
+    np.testing.assert_array_equal(wgu[1], [[1.0 + 0.5 * s, 0.5 + 0.5 * s],
+                                           [0.25 - 0.25 * s, 1.0 - 0.25 * s]])
+    # A_dn B_dn = [[2, 0]] ([n, d]); transposed onto W_dn [[1], [2]] ([d, n])
+    np.testing.assert_array_equal(wdn[1], [[1.0 + 2.0 * s], [2.0]])
+    # expert 0: every entry 3, so each delta entry is 3 * 3 (r = 1)
+    np.testing.assert_array_equal(wgu[0], np.full((2, 2), 3.0 + 9.0 * s))
+    np.testing.assert_array_equal(wdn[0], np.full((2, 1), 3.0 + 9.0 * s))
+    # at s = 1 the merged gate_up row gives the G of the hand example
+    if s == 1.0:
+        np.testing.assert_array_equal(np.array([1.0, 2.0]) @ wgu[1].T, [3.5, 1.5])
+
+
 def test_hand_combine_and_shared_expert():
     """Two routed experts with weights 3/4 and 1/4 plus a shared expert."""
     dims = LayerDims(1, 2, 1, 2, 2, 1, n_shared=1)
