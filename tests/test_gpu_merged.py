@@ -59,3 +59,41 @@ def test_merged_weights_and_forward(name):
     es = relerr(to_numpy_f64(y_s), ys_ref)
     print(f"merged Y {em:.2e}  split Y {es:.2e}", flush=True)
     assert em <= TOL and es <= TOL
+
+
+ALL4 = sum(1 << p for p in range(4))
+TILES = {
+    "256rows": mel.ENGINE_ALL | (ALL4 << 5),
+    "32k": mel.ENGINE_ALL | (ALL4 << 9),
+    "256rows_32k": mel.ENGINE_ALL | (ALL4 << 5) | (ALL4 << 9),
+    "register_path": 0,
+}
+
+
+@pytest.mark.parametrize("tiles", list(TILES.values()), ids=list(TILES))
+@pytest.mark.parametrize("name", ["ragged_shared_r3_s2", "wide_d320_zipf", "ragged_shared_r3_s2_f16"])
+def test_merged_forward_each_tile(name, tiles):
+    """The merged forward runs the streamed products without their low-rank
+    pass in whichever tile build the engine word selects for gate_up and down
+    (with the register path selected it still takes the default streamed
+    build)."""
+    require_gpu()
+    ld = CASES[name]
+    announce("merged tiles", f"{name} engines={tiles}", ld)
+    inp = make_inputs(ld, seed=6)
+    dims = mdims(ld)
+    logits, x, dy, w = upload(inp)
+    before = mel.get_engines(dims)
+    mel.set_engines(dims, tiles)
+    try:
+        rt = mel.route(logits, dims)
+        m = mel.merge_lora(w, dims)
+        y_m = mel.forward_merged(x, rt, m, dims, y=torch.full_like(x, float("nan")))
+        torch.cuda.synchronize()
+    finally:
+        mel.set_engines(dims, before)
+    ids, tw = oracle.topk_softmax(inp.logits, ld.k)
+    np.testing.assert_array_equal(rt.topk_ids.cpu().numpy(), ids)
+    em = relerr(to_numpy_f64(y_m), oracle.forward_merged(inp, ids, tw, ld))
+    print(f"merged Y {em:.2e}", flush=True)
+    assert em <= TOL
