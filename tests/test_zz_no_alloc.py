@@ -2,7 +2,8 @@
 callers that cannot allocate) against moe_route with a caller workspace,
 called through the C ABI: every routing output bit for bit, on two calls in a
 row (the second smaller, so it runs over what the first left in the scratch),
-and the host-side rejection of a shape whose scratch would exceed the limit."""
+recorded into a HIP graph and replayed, and the host-side rejection of a
+shape whose scratch would exceed the limit."""
 import ctypes
 
 import numpy as np
@@ -47,6 +48,38 @@ def _with_workspace(lib, dims, dc, logits):
                        torch.cuda.current_stream().cuda_stream)
     assert st == _lib.MOE_SUCCESS, _lib.status_string(st)
     return rt
+
+
+def test_noalloc_route_under_graph_capture():
+    """The callers it is for: moe_route_noalloc recorded into a HIP graph (in
+    a fresh process this is its first call, so its scratch lookup also runs
+    during the capture) and replayed three times, the outputs refilled with
+    sentinels before each replay; every replay bit for bit equal to moe_route
+    with a workspace."""
+    require_gpu()
+    lib = _lib.load()
+    ld = LayerDims(4096, 64, 64, 128, 8, 4)
+    announce("route_noalloc graph", ld)
+    dims, dc = _c(ld)
+    logits = torch.from_numpy(make_logits(ld, seed=30)).cuda()
+    ref = _with_workspace(lib, dims, dc, logits)
+    rt = _filled_routing(dims)
+    rc = _lib.MoeRouting(*[t.data_ptr() for t in rt])
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    status = []
+    with torch.cuda.graph(graph):
+        status.append(lib.moe_route_noalloc(ctypes.byref(dc), logits.data_ptr(), ctypes.byref(rc),
+                                            torch.cuda.current_stream().cuda_stream))
+    assert status == [_lib.MOE_SUCCESS], _lib.status_string(status[0])
+    for rep in range(3):
+        for t in rt:
+            t.fill_(-7)
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        for name, x, y in zip(mel.Routing._fields, rt, ref):
+            assert torch.equal(x.view(torch.int32), y.view(torch.int32)), (rep, name)
 
 
 CALLS = [
