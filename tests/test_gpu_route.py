@@ -1,7 +1,8 @@
 """Routing on the GPU against the oracle: top-k ids, counts, offsets,
 sorted_pair, pair_pos and the gather table's tokens bit-exact; routing weights
 (and the gather table's weights) to fp32 rounding; NaN and infinite logits
-give the oracle's ids."""
+give the oracle's ids.  The workloads, edge shapes, forced ties, non-finite
+rows, and 40 seeded random shapes and logit patterns."""
 import numpy as np
 import pytest
 import torch
@@ -102,3 +103,32 @@ def test_route_nan_and_infinite_logits():
     L[5] = -np.inf
     L[17::23, 5] = np.nan
     _run_and_compare(LayerDims(300, 64, 64, 24, 6, 4), L)
+
+
+def _random_route_case(i: int):
+    """Routing shape and logits of case i (fixed by i alone): T up to 40000,
+    E up to 256, k up to min(E, 16), the shared expert, a logit recipe, and
+    in some cases ties (logits rounded to a coarse grid) or non-finite values."""
+    g = np.random.default_rng(9000 + i)
+    E = int(g.choice([1, 2, 3, 7, 16, 31, 64, 100, 128, 200, 256]))
+    k = int(g.integers(1, min(E, 16) + 1))
+    recipes = ["normal", "bias", "zipf"] + (["stress"] if E >= 20 + k else [])
+    ld = LayerDims(T=int(g.choice([1, 5, 16, 17, 255, 1000, 4096, 9999, 40000])), d=64, n=64, E=E,
+                   k=k, r=4, n_shared=int(g.integers(0, 2)), logits_recipe=str(g.choice(recipes)))
+    L = make_logits(ld, seed=i)
+    mode = int(g.integers(0, 4))
+    if mode == 1:  # ties: many equal logits within a row
+        L = np.round(L * 2.0) / 2.0
+    elif mode == 2:  # scattered non-finite logits
+        m = g.random(L.shape)
+        L[m < 0.01] = np.nan
+        L[(m >= 0.01) & (m < 0.015)] = np.inf
+        L[(m >= 0.015) & (m < 0.02)] = -np.inf
+    return ld, L.astype(np.float32)
+
+
+@pytest.mark.parametrize("i", range(40))
+def test_route_random(i):
+    ld, L = _random_route_case(i)
+    announce("route random", i, ld)
+    _run_and_compare(ld, L)
