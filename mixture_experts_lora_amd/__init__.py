@@ -42,3 +42,4 @@ from .api import (  # noqa: F401
     workspace_bytes,
 )
 from ._lib import MOE_BF16, MOE_F16, MoeError, load  # noqa: F401
+from .autograd import moe_lora  # noqa: F401

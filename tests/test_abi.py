@@ -148,6 +148,11 @@ def test_python_binding_refuses_cpu_tensors():
     dims = mel.Dims(T=4, d=64, n=64, E=2, k=1, r=4)
     with pytest.raises(ValueError):
         mel.route(torch.zeros(4, 2), dims)
+    # the autograd wrapper goes through the same checks
+    w = mel.Weights(*(torch.zeros(s, dtype=torch.bfloat16) for s in
+                      ((2, 128, 64), (2, 64, 64), (2, 64, 4), (2, 4, 128), (2, 64, 4), (2, 4, 64))))
+    with pytest.raises(ValueError):
+        mel.moe_lora(torch.zeros(4, 64, dtype=torch.bfloat16), torch.zeros(4, 2), w, dims)
 
 
 def test_dims_struct_layout():
