@@ -34,6 +34,7 @@ class _MoELoRA(torch.autograd.Function):
         return y
 
     @staticmethod
+    @torch.autograd.function.once_differentiable
     def backward(ctx, dy):
         x, *w = ctx.saved_tensors
         dims, need = ctx.dims, ctx.needs_input_grad
