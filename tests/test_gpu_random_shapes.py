@@ -5,7 +5,6 @@ engine/tile setting inside the library's envelope, then runs route + forward
 with the float64 oracle built from the oracle's own routing (top-k ids bit
 for bit).  The draws are fixed by the case number, so a failing case can be
 run again by its id."""
-from dataclasses import replace
 
 import numpy as np
 import pytest
