@@ -492,6 +492,21 @@ def main():
     torch.cuda.synchronize()
     ms = t0.elapsed_time(t1) / args.steps
 
+    # the same step timed one at a time (each between its own pair of events),
+    # 50 of them after 10 more warm-ups: the distribution behind the mean
+    for _ in range(10):
+        step()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(50)]
+    for a, b in ev:
+        a.record()
+        step()
+        b.record()
+    torch.cuda.synchronize()
+    single = sorted(a.elapsed_time(b) for a, b in ev)
+    single_step = {"n": len(single), "median_ms": round(single[len(single) // 2], 4),
+                "p10_ms": round(single[len(single) // 10], 4),
+                "p90_ms": round(single[(9 * len(single)) // 10], 4)}
+
     # second timed region: the same steps with every kernel bracketed by events
     _lib.timing_enable(True)
     for _ in range(args.steps):
@@ -597,6 +612,7 @@ def main():
         "steps": args.steps,
         "warmup": args.warmup,
         "ms_per_step": ms,
+        "single_step_ms": single_step,
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
